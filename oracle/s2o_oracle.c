@@ -1,0 +1,387 @@
+/*
+ * CPU oracle for S2O causal-prefill attention -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may load
+ * this library.  The product path never calls it; it shares no source, header,
+ * table or helper with the HIP library.  It is plain, slow and written to be
+ * checked against the pages by eye.
+ *
+ * Sources (all about "S2O: Early Stopping for Sparse Attention via Online
+ * Permutation", Zhang et al., arXiv 2602.22575):
+ *   [ABS]  the authors' abstract, as reproduced on the pith.science page
+ *          ("read the original abstract").
+ *   [GIST] the gist.science technical summary (French), section "Méthodologie :
+ *          S2O": "1. Permutation en ligne via Chargement Guidé par Index"
+ *          (Classement par Segment, KV_perm, Chargement Planifié par
+ *          Coordonnées), "2. Règle d'Arrêt Anticipé", "3. Implémentation du
+ *          Noyau" (Passage 1, Passage 2).
+ *   [LENS] the arxivlens summary (Methodology and Limitations facets).
+ *
+ * What is computed, per (batch b, query head h, query tile t of BM rows):
+ *   geometry   segments of S tokens; tile t starts at row t*BM; its segment
+ *              starts at a_t = floor(t*BM/S)*S; its history is keys [0, a_t).
+ *              [GIST] "Classement par Segment".
+ *   pool       qbar[k] = (sum over the tile's BM rows, ascending, in fp32) * 2^-log2(BM)
+ *              -- the tile's representative query.  The pages leave the
+ *              representative unspecified ([GIST] KV_perm); the mean of the
+ *              tile's rows is the reading taken here.
+ *   score      s[j] = fp32 dot(qbar, K[b, h/G, j]) for j < a_t, accumulated
+ *              with one fmaf per dimension in ascending order (the canonical
+ *              order, part of the definition so that any faithful evaluation
+ *              gives the same bits).  Only causal-prefix keys are scored
+ *              ([GIST] KV_perm).
+ *   order      the list: history keys sorted by score descending, ties to the
+ *              lower index ([GIST] KV_perm: indices form a global logical map).
+ *   pass 1     for each row i, online softmax over keys [a_t, i] in BN-wide key
+ *              tiles in ascending order ([GIST] Passage 1: dense causal window
+ *              inside the current segment, initialising (m, l, acc)).
+ *   pass 2     for chunk c = 0, 1, ... of BN consecutive list entries: the same
+ *              online update with no mask (every history key precedes every
+ *              row), then the chunk's marginal mass gain
+ *              delta_i = sum_{j in chunk} exp(x_ij - m_i) and the ratio
+ *              g_i = delta_i / l_i (l_i after adding the chunk).  Stop after
+ *              chunk c when max_i g_i < tau ([GIST] "2. Règle d'Arrêt
+ *              Anticipé": stop once the marginal gain falls below a threshold
+ *              relative to the accumulated score; [ABS]: proceed from high to
+ *              low importance and skip the remaining blocks; [GIST] Passage 2).
+ *              The chunk that triggers the stop is kept; the comparison is
+ *              strict, so tau = 0 never stops.
+ *   output     O_i = acc_i / l_i; executed tiles = pass-1 key tiles + executed
+ *              pass-2 chunks.
+ *
+ * Precision: the estimator (pool, score) is fp32 in the canonical order above;
+ * the attention itself is evaluated in fp64.  bf16 inputs are widened exactly.
+ * Build with -ffp-contract=off so that no multiply-add is fused except the
+ * explicit fmaf calls.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int32_t B, Hq, Hkv, N, d;
+    int32_t dtype; /* 0: fp32 values, 1: bf16 bit patterns (uint16) */
+    int32_t seg_len, tile_m, tile_n;
+    double scale;
+} oracle_problem;
+
+/* ---- element access ------------------------------------------------------ */
+
+static float widen(const void *base, int32_t dtype, int64_t i) {
+    if (dtype == 0) return ((const float *)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+static int64_t q_index(const oracle_problem *p, int b, int h, int64_t row, int k) {
+    return (((int64_t)b * p->Hq + h) * p->N + row) * p->d + k;
+}
+
+static int64_t kv_index(const oracle_problem *p, int b, int g, int64_t row, int k) {
+    return (((int64_t)b * p->Hkv + g) * p->N + row) * p->d + k;
+}
+
+/* ---- geometry ([GIST] Classement par Segment) ----------------------------- */
+
+int32_t oracle_num_tiles(const oracle_problem *p) { return p->N / p->tile_m; }
+
+int64_t oracle_seg_start(const oracle_problem *p, int t) {
+    int64_t first_row = (int64_t)t * p->tile_m;
+    return (first_row / p->seg_len) * p->seg_len;
+}
+
+/* number of BN-wide key tiles in pass 1: keys [a_t, (t+1)*BM) */
+int32_t oracle_pass1_tiles(const oracle_problem *p, int t) {
+    int64_t a = oracle_seg_start(p, t);
+    int64_t end = (int64_t)(t + 1) * p->tile_m;
+    return (int32_t)((end - a + p->tile_n - 1) / p->tile_n);
+}
+
+/* Offsets of the per-tile lists, ordered by (b, h, t).  Computed by walking
+ * the tiles and adding their history lengths; lists of segment-0 tiles are
+ * empty. */
+int64_t oracle_list_offset(const oracle_problem *p, int b, int h, int t) {
+    int32_t T = oracle_num_tiles(p);
+    int64_t per_head = 0;
+    for (int u = 0; u < T; ++u) per_head += oracle_seg_start(p, u);
+    int64_t off = ((int64_t)b * p->Hq + h) * per_head;
+    for (int u = 0; u < t; ++u) off += oracle_seg_start(p, u);
+    return off;
+}
+
+int64_t oracle_list_entries(const oracle_problem *p) {
+    return oracle_list_offset(p, p->B - 1, p->Hq - 1, oracle_num_tiles(p) - 1) +
+           oracle_seg_start(p, oracle_num_tiles(p) - 1);
+}
+
+/* ---- estimator: pool and score ------------------------------------------- */
+
+/* Representative query of tile t: the mean of its BM rows (fp32 sum in
+ * ascending row order, then an exact power-of-two scaling; BM must be a power
+ * of two). */
+void oracle_pool(const oracle_problem *p, const void *Q, int b, int h, int t, float *qbar) {
+    float inv = 1.0f / (float)p->tile_m; /* exact for powers of two */
+    for (int k = 0; k < p->d; ++k) {
+        float sum = 0.0f;
+        for (int r = 0; r < p->tile_m; ++r)
+            sum = sum + widen(Q, p->dtype, q_index(p, b, h, (int64_t)t * p->tile_m + r, k));
+        qbar[k] = sum * inv;
+    }
+}
+
+/* Scores of tile t's history keys: s[j] = fmaf chain over k = 0..d-1. */
+void oracle_score_tile(const oracle_problem *p, const void *Q, const void *K, int b, int h,
+                       int t, float *scores) {
+    int g = h / (p->Hq / p->Hkv);
+    int64_t a = oracle_seg_start(p, t);
+    float *qbar = (float *)malloc(sizeof(float) * p->d);
+    oracle_pool(p, Q, b, h, t, qbar);
+    for (int64_t j = 0; j < a; ++j) {
+        float acc = 0.0f;
+        for (int k = 0; k < p->d; ++k) acc = fmaf(qbar[k], widen(K, p->dtype, kv_index(p, b, g, j, k)), acc);
+        scores[j] = acc;
+    }
+    free(qbar);
+}
+
+/* ---- order: history keys by score descending, ties to the lower index ---- */
+
+typedef struct {
+    float s;
+    int32_t j;
+} scored_key;
+
+static int by_score_desc_then_index(const void *x, const void *y) {
+    const scored_key *a = (const scored_key *)x, *c = (const scored_key *)y;
+    if (a->s > c->s) return -1;
+    if (a->s < c->s) return 1; /* -0.0 and +0.0 compare equal: a tie */
+    return (a->j > c->j) - (a->j < c->j);
+}
+
+void oracle_order(const float *scores, int64_t n, int32_t *list) {
+    scored_key *tmp = (scored_key *)malloc(sizeof(scored_key) * (n > 0 ? n : 1));
+    for (int64_t j = 0; j < n; ++j) {
+        tmp[j].s = scores[j];
+        tmp[j].j = (int32_t)j;
+    }
+    qsort(tmp, (size_t)n, sizeof(scored_key), by_score_desc_then_index);
+    for (int64_t j = 0; j < n; ++j) list[j] = tmp[j].j;
+    free(tmp);
+}
+
+/* ---- attention: pass 1 + pass 2 with early stop -------------------------- */
+
+typedef struct {
+    double m, l;
+    double *acc;
+} row_state;
+
+/* logit x_ij = scale * dot(Q_i, K_j) in double */
+static double logit(const oracle_problem *p, const void *Q, const void *K, int b, int h, int g,
+                    int64_t i, int64_t j) {
+    double dot = 0.0;
+    for (int k = 0; k < p->d; ++k)
+        dot += (double)widen(Q, p->dtype, q_index(p, b, h, i, k)) *
+               (double)widen(K, p->dtype, kv_index(p, b, g, j, k));
+    return p->scale * dot;
+}
+
+/* Online-softmax update of one row with a set of keys; returns the set's mass
+ * sum_j exp(x_ij - m_new) measured against the updated running max. */
+static double absorb(const oracle_problem *p, const void *Q, const void *K, const void *V,
+                     int b, int h, int g, int64_t i, const int64_t *keys, int nkeys,
+                     row_state *st, double *x) {
+    double m_new = st->m;
+    for (int e = 0; e < nkeys; ++e) {
+        x[e] = logit(p, Q, K, b, h, g, i, keys[e]);
+        if (x[e] > m_new) m_new = x[e];
+    }
+    double rescale = exp(st->m - m_new); /* exp(-inf) = 0 on the first update */
+    double mass = 0.0;
+    st->l *= rescale;
+    for (int k = 0; k < p->d; ++k) st->acc[k] *= rescale;
+    for (int e = 0; e < nkeys; ++e) {
+        double w = exp(x[e] - m_new);
+        mass += w;
+        for (int k = 0; k < p->d; ++k) st->acc[k] += w * (double)widen(V, p->dtype, kv_index(p, b, g, keys[e], k));
+    }
+    st->l += mass;
+    st->m = m_new;
+    return mass;
+}
+
+/*
+ * One query tile.  `list` holds the tile's a_t history indices in visiting
+ * order.  tau >= 0.  force_n > 0 executes exactly min(force_n, C_t) pass-2
+ * chunks regardless of tau (used to re-check a tile at a given chunk count).
+ * Outputs: out[BM*d] in double, *n_exec = pass-1 tiles + executed chunks,
+ * gstar[c] = max_i g_i of chunk c for the executed chunks (may be NULL).
+ * Returns the number of executed pass-2 chunks.
+ */
+int32_t oracle_attn_tile(const oracle_problem *p, const void *Q, const void *K, const void *V,
+                         int b, int h, int t, const int32_t *list, double tau, int32_t force_n,
+                         double *out, int32_t *n_exec, double *gstar) {
+    int BM = p->tile_m, BN = p->tile_n, d = p->d;
+    int g = h / (p->Hq / p->Hkv);
+    int64_t row0 = (int64_t)t * BM;
+    int64_t a = oracle_seg_start(p, t);
+    int32_t chunks = (int32_t)(a / BN);
+    row_state *st = (row_state *)malloc(sizeof(row_state) * BM);
+    double *accs = (double *)calloc((size_t)BM * d, sizeof(double));
+    double *x = (double *)malloc(sizeof(double) * BN);
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * BN);
+    for (int r = 0; r < BM; ++r) {
+        st[r].m = -INFINITY;
+        st[r].l = 0.0;
+        st[r].acc = accs + (size_t)r * d;
+    }
+
+    /* pass 1: contiguous key tiles of the current segment, causal mask */
+    int32_t p1 = oracle_pass1_tiles(p, t);
+    for (int32_t c = 0; c < p1; ++c) {
+        int64_t k0 = a + (int64_t)c * BN;
+        for (int r = 0; r < BM; ++r) {
+            int64_t i = row0 + r;
+            int n = 0;
+            for (int e = 0; e < BN; ++e)
+                if (k0 + e <= i) keys[n++] = k0 + e;
+            if (n > 0) absorb(p, Q, K, V, b, h, g, i, keys, n, &st[r], x);
+        }
+    }
+
+    /* pass 2: list chunks in order, early stop on the marginal gain */
+    int32_t executed = 0;
+    int32_t limit = (force_n > 0 && force_n < chunks) ? force_n : chunks;
+    for (int32_t c = 0; c < limit; ++c) {
+        for (int e = 0; e < BN; ++e) keys[e] = list[(int64_t)c * BN + e];
+        double worst = 0.0; /* max over rows of g_i */
+        for (int r = 0; r < BM; ++r) {
+            double mass = absorb(p, Q, K, V, b, h, g, row0 + r, keys, BN, &st[r], x);
+            double gain = mass / st[r].l;
+            if (gain > worst) worst = gain;
+        }
+        if (gstar) gstar[c] = worst;
+        executed = c + 1;
+        if (force_n <= 0 && worst < tau) break;
+    }
+
+    for (int r = 0; r < BM; ++r)
+        for (int k = 0; k < d; ++k) out[(size_t)r * d + k] = st[r].acc[k] / st[r].l;
+    *n_exec = p1 + executed;
+    free(keys);
+    free(x);
+    free(accs);
+    free(st);
+    return executed;
+}
+
+/* Dense causal softmax attention for rows [i0, i1) of (b, h), in double. */
+void oracle_dense_rows(const oracle_problem *p, const void *Q, const void *K, const void *V,
+                       int b, int h, int64_t i0, int64_t i1, double *out) {
+    int g = h / (p->Hq / p->Hkv);
+    double *x = (double *)malloc(sizeof(double) * p->N);
+    for (int64_t i = i0; i < i1; ++i) {
+        double mx = -INFINITY, den = 0.0;
+        for (int64_t j = 0; j <= i; ++j) {
+            x[j] = logit(p, Q, K, b, h, g, i, j);
+            if (x[j] > mx) mx = x[j];
+        }
+        double *o = out + (size_t)(i - i0) * p->d;
+        for (int k = 0; k < p->d; ++k) o[k] = 0.0;
+        for (int64_t j = 0; j <= i; ++j) {
+            double w = exp(x[j] - mx);
+            den += w;
+            for (int k = 0; k < p->d; ++k) o[k] += w * (double)widen(V, p->dtype, kv_index(p, b, g, j, k));
+        }
+        for (int k = 0; k < p->d; ++k) o[k] /= den;
+    }
+    free(x);
+}
+
+/* ---- whole problems and tile samples (OpenMP over tiles) ----------------- */
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* scores of every tile, in the (b, h, t) list layout */
+void oracle_scores_all(const oracle_problem *p, const void *Q, const void *K, float *scores) {
+    int32_t T = oracle_num_tiles(p);
+    int64_t units = (int64_t)p->B * p->Hq * T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int b = (int)(u / ((int64_t)p->Hq * T)), h = (int)((u / T) % p->Hq), t = (int)(u % T);
+        if (oracle_seg_start(p, t) > 0)
+            oracle_score_tile(p, Q, K, b, h, t, scores + oracle_list_offset(p, b, h, t));
+    }
+}
+
+/* lists of every tile from the scores */
+void oracle_lists_all(const oracle_problem *p, const float *scores, int32_t *lists) {
+    int32_t T = oracle_num_tiles(p);
+    int64_t units = (int64_t)p->B * p->Hq * T;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        int b = (int)(u / ((int64_t)p->Hq * T)), h = (int)((u / T) % p->Hq), t = (int)(u % T);
+        int64_t off = oracle_list_offset(p, b, h, t);
+        oracle_order(scores + off, oracle_seg_start(p, t), lists + off);
+    }
+}
+
+/*
+ * A set of tiles, each given as (b, h, t) in tiles[3*n..3*n+2].  For each:
+ * scores, list, pass 1 and pass 2.  `lists_in` (may be NULL) supplies the full
+ * list buffer in the (b, h, t) layout; when NULL the tile's list is computed
+ * here.  Outputs per tile n: out[n*BM*d ...] (double), n_exec[n], chunks[n];
+ * gstar (may be NULL) has room for max_chunks entries per tile; list_out (may
+ * be NULL) receives each tile's list at offset n*max_list.
+ * force_n (may be NULL) gives a per-tile forced chunk count (0 = use tau).
+ */
+void oracle_attn_tiles(const oracle_problem *p, const void *Q, const void *K, const void *V,
+                       const int32_t *tiles, int64_t n_tiles, const int32_t *lists_in,
+                       double tau, const int32_t *force_n, double *out, int32_t *n_exec,
+                       int32_t *chunks, double *gstar, int64_t max_chunks, int32_t *list_out,
+                       int64_t max_list) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_tiles; ++n) {
+        int b = tiles[3 * n], h = tiles[3 * n + 1], t = tiles[3 * n + 2];
+        int64_t a = oracle_seg_start(p, t);
+        int32_t *list;
+        int32_t *owned = NULL;
+        if (lists_in) {
+            list = (int32_t *)lists_in + oracle_list_offset(p, b, h, t);
+        } else {
+            float *s = (float *)malloc(sizeof(float) * (a > 0 ? a : 1));
+            owned = (int32_t *)malloc(sizeof(int32_t) * (a > 0 ? a : 1));
+            if (a > 0) oracle_score_tile(p, Q, K, b, h, t, s);
+            oracle_order(s, a, owned);
+            free(s);
+            list = owned;
+        }
+        if (list_out)
+            for (int64_t j = 0; j < a; ++j) list_out[n * max_list + j] = list[j];
+        chunks[n] = oracle_attn_tile(p, Q, K, V, b, h, t, list, tau, force_n ? force_n[n] : 0,
+                                     out + (size_t)n * p->tile_m * p->d, &n_exec[n],
+                                     gstar ? gstar + n * max_chunks : NULL);
+        free(owned);
+    }
+}
+
+/* dense rows for a set of (b, h, i0, i1) requests, out packed in order */
+void oracle_dense_requests(const oracle_problem *p, const void *Q, const void *K, const void *V,
+                           const int64_t *req, int64_t n_req, const int64_t *out_off, double *out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_req; ++n)
+        oracle_dense_rows(p, Q, K, V, (int)req[4 * n], (int)req[4 * n + 1], req[4 * n + 2],
+                          req[4 * n + 3], out + out_off[n]);
+}

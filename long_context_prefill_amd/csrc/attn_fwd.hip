@@ -1,0 +1,464 @@
+// Gathered FlashAttention-style forward for gfx950, dense and S2O schedules.
+//
+// Method: "S2O: Early Stopping for Sparse Attention via Online Permutation"
+// (gist.science technical summary, "3. Implémentation du Noyau": pass 1 is a
+// dense causal window inside the current segment that initialises the online
+// softmax state (m, l, acc); pass 2 resumes that state and walks the history
+// keys in the order of the tile's index list, gathering K/V rows by index
+// ("Chargement Planifié par Coordonnées"), and stops early on the marginal
+// gain ("2. Règle d'Arrêt Anticipé").  The two passes are fused here: one
+// workgroup runs both for its query tile, keeping (m, l, acc) in registers.
+//
+// Mapping to CDNA4:
+//   * one workgroup per (b, query head, query tile of BM = 32*NW rows); each
+//     wave owns 32 query rows;
+//   * S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 (fp32 problems:
+//     v_mfma_f32_32x32x2_f32) so that in the 32x32 accumulator layout every
+//     lane holds 16 keys of ONE query row: row statistics need one exchange
+//     with the partner lane (lane ^ 32) instead of a cross-lane tree;
+//   * the same layout makes the probabilities directly usable as the B
+//     operand of O^T = V^T P^T, so P never leaves registers;
+//   * K/V chunks of 64 keys are staged through LDS, double-buffered, with
+//     the next chunk's rows fetched into registers while the current chunk
+//     computes.  Gathered rows are read 256 contiguous bytes per row by
+//     consecutive lanes; V is written to LDS transposed (keys innermost) so
+//     the PV operand reads are contiguous;
+//   * the stop decision is uniform per workgroup: each wave ballots whether
+//     any of its rows still gains >= tau, the waves exchange one flag each
+//     through LDS at the barrier that already separates the LDS buffers;
+//   * work order is heaviest-first (late tiles first) and the G query heads
+//     sharing one KV head are placed on the same XCD so they share its L2.
+#include "s2o_internal.h"
+
+namespace s2o {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct AttnParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    void *o;
+    const int32_t *idx;
+    int32_t *exec;
+    Geometry g;
+    float scale_log2;  // softmax scale * log2(e)
+    float tau;
+};
+
+// Block -> (b, h, t).  Units (b, kv head, t) are ordered t-descending; the G
+// query heads of a unit get block ids congruent mod 8, i.e. the same XCD.
+struct Work {
+    int b, h, t;
+};
+
+__device__ inline bool map_block(const Geometry &g, Work &w) {
+    int bid = blockIdx.x;
+    int x = bid & 7, r = bid >> 3;
+    int hq = r % g.G;
+    int u = 8 * (r / g.G) + x;
+    int units = g.B * g.Hkv * g.T;
+    if (u >= units) return false;
+    int per_t = g.B * g.Hkv;
+    w.t = g.T - 1 - u / per_t;
+    int rem = u % per_t;
+    w.b = rem / g.Hkv;
+    w.h = (rem % g.Hkv) * g.G + hq;
+    return true;
+}
+
+__device__ inline float partner(float x) { return __shfl_xor(x, 32); }
+
+__device__ inline float max16(const f32x16 &v) {
+    float m = v[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) m = fmaxf(m, v[r]);
+    return m;
+}
+
+// Causal mask on a diagonal chunk.  Register r of block blk holds key
+// key0 + 32*blk + 8*(r/4) + 4*half + r%4 for this lane's query row.
+__device__ inline void mask_chunk(f32x16 &s0, f32x16 &s1, int key0, int row, int half) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        int kk = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (kk > row) s0[r] = -INFINITY;
+        if (kk + 32 > row) s1[r] = -INFINITY;
+    }
+}
+
+// Online-softmax update of one chunk for this lane's row.  Turns s0/s1 into
+// probabilities exp2(s*c - m_new); returns the chunk mass delta (against
+// m_new) and the rescale factor of the old state.
+__device__ inline void softmax_chunk(f32x16 &s0, f32x16 &s1, float c, float &m, float &l,
+                                     float &alpha, float &delta) {
+    float mx = fmaxf(max16(s0), max16(s1));
+    mx = fmaxf(mx, partner(mx));
+    float m_new = fmaxf(m, mx * c);
+    alpha = exp2f(m - m_new);  // 0 on the first chunk (m = -inf)
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        s0[r] = exp2f(fmaf(s0[r], c, -m_new));
+        s1[r] = exp2f(fmaf(s1[r], c, -m_new));
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += s0[r] + s1[r];
+    sum += partner(sum);
+    delta = sum;
+    l = l * alpha + sum;
+    m = m_new;
+}
+
+template <int NACC>
+__device__ inline void rescale(f32x16 (&acc)[NACC], float alpha) {
+    // skip when no row of the wave changed its max (common once the list's
+    // largest keys have been seen)
+    if (__ballot(alpha != 1.0f) == 0) return;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+}
+
+__device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+// Position of chunk key j (0..63) inside a transposed-V row: within each group
+// of 16 keys, j = 8q + 4h + e is stored at 8h + 4q + e, so the 8 keys a lane
+// half feeds to one MFMA step are contiguous.
+__device__ inline int vpos(int j) {
+    return (j & ~15) | ((j & 4) << 1) | ((j & 8) >> 1) | (j & 3);
+}
+
+template <typename T, int D, int NW, bool S2O>
+struct Cfg {
+    static constexpr bool kBf16 = sizeof(T) == 2;
+    static constexpr int BM = 32 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BN = kTileN;
+    // LDS row strides in elements (padding chosen for conflict-free MFMA
+    // operand reads and transposed writes)
+    static constexpr int KSTR = kBf16 ? D + 8 : D + 2;
+    static constexpr int VROWS = kBf16 ? D : BN;           // V^T rows (bf16) or V rows (fp32)
+    static constexpr int VSTR = kBf16 ? BN + 4 : D + 8;
+    static constexpr int KBUF = BN * KSTR;
+    static constexpr int VBUF = VROWS * VSTR;
+    static constexpr int BUF = KBUF + VBUF;                 // elements per stage
+    static constexpr size_t LDS_BYTES = 2 * BUF * sizeof(T);
+    // global -> register staging
+    static constexpr int EPV = 16 / sizeof(T);              // elements per 16-byte piece
+    static constexpr int KPIECES = BN * D / EPV / NT;       // K pieces per thread
+    // bf16: V is loaded as row pairs (two 16-byte pieces) and transposed;
+    // fp32: V is loaded like K.
+    static constexpr int VITEMS = kBf16 ? (BN / 2) * (D / 8) / NT : KPIECES;
+    static_assert(KPIECES >= 1 && VITEMS >= 1, "tile too small for the thread count");
+};
+
+template <typename T, int D, int NW, bool S2O>
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel(AttnParams a) {
+    using C = Cfg<T, D, NW, S2O>;
+    constexpr int BM = C::BM, NT = C::NT, BN = C::BN;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    T *lds = reinterpret_cast<T *>(smem_raw);
+    __shared__ int flags[2][NW];
+
+    const Geometry &g = a.g;
+    Work wk;
+    if (!map_block(g, wk)) return;
+    const int b = wk.b, h = wk.h, t = wk.t;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, half = lane >> 5;
+    const int row0 = t * BM;
+    const int my_row = row0 + 32 * wave + li;
+    const int wave_last_row = row0 + 32 * wave + 31;
+
+    // schedule: pass-1 chunks are contiguous key tiles starting at base1; pass-2
+    // chunks are consecutive BN-entry slices of the tile's list
+    const int seg_a = S2O ? (int)seg_start(g, t) : 0;
+    const int base1 = seg_a;
+    const int n1 = g.causal ? (row0 + BM - base1) / BN : g.N / BN;
+    const int n2 = S2O ? seg_a / BN : 0;
+    const int total = n1 + n2;
+    const int32_t *list = S2O ? a.idx + list_offset(g, b, h, t) : nullptr;
+
+    const int kvh = h / g.G;
+    const T *Qp = reinterpret_cast<const T *>(a.q) + ((int64_t)(b * g.Hq + h) * g.N) * D;
+    const T *Kp = reinterpret_cast<const T *>(a.k) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
+    const T *Vp = reinterpret_cast<const T *>(a.v) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
+
+    auto chunk_row = [&](int k, int p) -> int {
+        return k < n1 ? base1 + k * BN + p : list[(k - n1) * BN + p];
+    };
+
+    // ---- per-thread staging geometry
+    constexpr int KCG = D / C::EPV;  // 16-byte pieces per row
+    int krow_p[C::KPIECES], kcg[C::KPIECES];
+#pragma unroll
+    for (int i = 0; i < C::KPIECES; ++i) {
+        int pc = i * NT + tid;
+        krow_p[i] = pc / KCG;
+        kcg[i] = pc % KCG;
+    }
+    int vrow_p[C::VITEMS], vcg[C::VITEMS];
+#pragma unroll
+    for (int i = 0; i < C::VITEMS; ++i) {
+        int I = i * NT + tid;
+        if constexpr (C::kBf16) {
+            vrow_p[i] = 2 * ((I >> 2) & 31);       // first row of the pair
+            vcg[i] = 4 * (I >> 7) + (I & 3);       // 8-column group
+        } else {
+            vrow_p[i] = I / KCG;
+            vcg[i] = I % KCG;
+        }
+    }
+    int krow[C::KPIECES], vrow[C::VITEMS][2];
+    u32x4 kreg[C::KPIECES], vreg[C::VITEMS][2];
+
+    auto fetch_rows = [&](int k) {
+#pragma unroll
+        for (int i = 0; i < C::KPIECES; ++i) krow[i] = chunk_row(k, krow_p[i]);
+#pragma unroll
+        for (int i = 0; i < C::VITEMS; ++i) {
+            vrow[i][0] = chunk_row(k, vrow_p[i]);
+            if constexpr (C::kBf16) vrow[i][1] = chunk_row(k, vrow_p[i] + 1);
+        }
+    };
+    auto issue_loads = [&]() {
+#pragma unroll
+        for (int i = 0; i < C::KPIECES; ++i)
+            kreg[i] = *reinterpret_cast<const u32x4 *>(Kp + (int64_t)krow[i] * D + kcg[i] * C::EPV);
+#pragma unroll
+        for (int i = 0; i < C::VITEMS; ++i) {
+            vreg[i][0] = *reinterpret_cast<const u32x4 *>(Vp + (int64_t)vrow[i][0] * D + vcg[i] * C::EPV);
+            if constexpr (C::kBf16)
+                vreg[i][1] = *reinterpret_cast<const u32x4 *>(Vp + (int64_t)vrow[i][1] * D + vcg[i] * 8);
+        }
+    };
+    auto store_lds = [&](int buf) {
+        T *Kl = lds + buf * C::BUF;
+        T *Vl = Kl + C::KBUF;
+#pragma unroll
+        for (int i = 0; i < C::KPIECES; ++i) {
+            T *dst = Kl + krow_p[i] * C::KSTR + kcg[i] * C::EPV;
+            if constexpr (C::kBf16) {
+                *reinterpret_cast<u32x4 *>(dst) = kreg[i];
+            } else {  // fp32 rows are only 8-byte aligned
+                reinterpret_cast<u32x2 *>(dst)[0] = kreg[i].xy;
+                reinterpret_cast<u32x2 *>(dst)[1] = kreg[i].zw;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::VITEMS; ++i) {
+            if constexpr (C::kBf16) {
+                // transpose a 2x8 block: V[j][c], V[j+1][c] -> V^T[c][vpos(j)] (4 bytes)
+                const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
+                const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+                uint16_t *Vt = reinterpret_cast<uint16_t *>(Vl);
+                int pos = vpos(vrow_p[i]);
+                int c0 = vcg[i] * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t pk = (e & 1) ? pack_hi(w0[e >> 1], w1[e >> 1]) : pack_lo(w0[e >> 1], w1[e >> 1]);
+                    *reinterpret_cast<uint32_t *>(Vt + (c0 + e) * C::VSTR + pos) = pk;
+                }
+            } else {
+                *reinterpret_cast<u32x4 *>(Vl + vrow_p[i] * C::VSTR + vcg[i] * 4) = vreg[i][0];
+            }
+        }
+    };
+
+    // ---- Q operand in registers (B operand of S^T = K Q^T)
+    constexpr int QSTEPS = C::kBf16 ? D / 16 : D / 2;
+    using QReg = typename std::conditional<C::kBf16, bf16x8, float>::type;
+    QReg qf[QSTEPS];
+#pragma unroll
+    for (int s = 0; s < QSTEPS; ++s) {
+        if constexpr (C::kBf16)
+            qf[s] = *reinterpret_cast<const bf16x8 *>(Qp + (int64_t)my_row * D + 16 * s + 8 * half);
+        else
+            qf[s] = Qp[(int64_t)my_row * D + 2 * s + half];
+    }
+
+    constexpr int NACC = D / 32;
+    f32x16 acc[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const float c = a.scale_log2;
+
+    // prologue: chunk 0 -> LDS stage 0, rows of chunk 1 in registers
+    fetch_rows(0);
+    issue_loads();
+    if (total > 1) fetch_rows(1);
+    store_lds(0);
+    __syncthreads();
+
+    int executed2 = 0;
+    for (int k = 0; k < total; ++k) {
+        const int buf = k & 1;
+        const bool has_next = k + 1 < total;
+        if (has_next) {
+            issue_loads();
+            if (k + 2 < total) fetch_rows(k + 2);
+        }
+        const T *Kl = lds + buf * C::BUF;
+        const T *Vl = Kl + C::KBUF;
+        const bool is_p2 = S2O && k >= n1;
+        const int key0 = is_p2 ? 0 : base1 + k * BN;
+        bool wave_cont = false;
+        // a wave whose rows all precede the chunk has nothing to add
+        const bool skip = !is_p2 && g.causal && key0 > wave_last_row;
+        if (!skip) {
+            f32x16 s0, s1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+            if constexpr (C::kBf16) {
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) {
+                    bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 16 * s + 8 * half);
+                    bf16x8 kb = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 16 * s + 8 * half);
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s], s1, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < D / 2; ++s) {
+                    float ka = Kl[li * C::KSTR + 2 * s + half];
+                    float kb = Kl[(32 + li) * C::KSTR + 2 * s + half];
+                    s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kb, qf[s], s1, 0, 0, 0);
+                }
+            }
+            if (!is_p2 && g.causal && key0 + BN - 1 > row0 + 32 * wave) mask_chunk(s0, s1, key0, my_row, half);
+            float alpha, delta;
+            softmax_chunk(s0, s1, c, m, l, alpha, delta);
+            if (is_p2) wave_cont = __ballot(!(delta < a.tau * l)) != 0;
+            rescale(acc, alpha);
+            // O^T += V^T P^T
+            if constexpr (C::kBf16) {
+                bf16x8 pb[4];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pb[0][e] = (__bf16)s0[e];
+                    pb[1][e] = (__bf16)s0[8 + e];
+                    pb[2][e] = (__bf16)s1[e];
+                    pb[3][e] = (__bf16)s1[8 + e];
+                }
+                const uint16_t *Vt = reinterpret_cast<const uint16_t *>(Vl);
+#pragma unroll
+                for (int cb = 0; cb < NACC; ++cb) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const uint16_t *src = Vt + (32 * cb + li) * C::VSTR + 16 * s + 8 * half;
+                        u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
+                        u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 4);
+                        bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < NACC; ++cb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        int j = 8 * (r >> 2) + 4 * half + (r & 3);
+                        float v0 = Vl[j * C::VSTR + 32 * cb + li];
+                        float v1 = Vl[(32 + j) * C::VSTR + 32 * cb + li];
+                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, s0[r], acc[cb], 0, 0, 0);
+                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, s1[r], acc[cb], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        if (has_next) store_lds(buf ^ 1);
+        if (is_p2 && lane == 0) flags[buf][wave] = wave_cont ? 1 : 0;
+        __syncthreads();
+        if (is_p2) {
+            executed2 = k - n1 + 1;
+            int any = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) any |= flags[buf][w];
+            if (!any) break;
+        }
+    }
+
+    // epilogue: O = acc / l; lane holds O[my_row][32cb + 8q + 4half + 0..3]
+    const float inv = 1.0f / l;
+    T *Op = reinterpret_cast<T *>(a.o) + ((int64_t)(b * g.Hq + h) * g.N + my_row) * D;
+#pragma unroll
+    for (int cb = 0; cb < NACC; ++cb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            T *dst = Op + 32 * cb + 8 * q + 4 * half;
+            if constexpr (C::kBf16) {
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][4 * q + e] * inv));
+                *reinterpret_cast<u32x2 *>(dst) = u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+            } else {
+                float4 o4 = make_float4(acc[cb][4 * q] * inv, acc[cb][4 * q + 1] * inv,
+                                        acc[cb][4 * q + 2] * inv, acc[cb][4 * q + 3] * inv);
+                *reinterpret_cast<float4 *>(dst) = o4;
+            }
+        }
+    }
+    if (a.exec && tid == 0) a.exec[((int64_t)b * g.Hq + h) * g.T + t] = n1 + executed2;
+}
+
+template <typename T, int D, int NW, bool S2O>
+hipError_t launch_one(const AttnParams &p, hipStream_t stream) {
+    using C = Cfg<T, D, NW, S2O>;
+    const Geometry &g = p.g;
+    static bool attr_set = false;  // benign race: setting the same value twice is harmless
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<T, D, NW, S2O>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    int64_t units = (int64_t)g.B * g.Hkv * g.T;
+    int64_t blocks = ((units + 7) / 8) * 8 * g.G;
+    hipLaunchKernelGGL((attn_kernel<T, D, NW, S2O>), dim3((unsigned)blocks), dim3(C::NT),
+                       C::LDS_BYTES, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool S2O>
+hipError_t launch_bm(const AttnParams &p, hipStream_t s) {
+    return p.g.BM == 128 ? launch_one<T, D, 4, S2O>(p, s) : launch_one<T, D, 2, S2O>(p, s);
+}
+
+template <typename T, bool S2O>
+hipError_t launch_d(const AttnParams &p, hipStream_t s) {
+    return p.g.d == 128 ? launch_bm<T, 128, S2O>(p, s) : launch_bm<T, 64, S2O>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_attention(const Geometry &g, const void *Q, const void *K, const void *V,
+                            const int32_t *idx, float tau, void *O, int32_t *exec_tiles,
+                            bool s2o, hipStream_t stream) {
+    AttnParams p;
+    p.q = Q;
+    p.k = K;
+    p.v = V;
+    p.o = O;
+    p.idx = idx;
+    p.exec = exec_tiles;
+    p.g = g;
+    p.scale_log2 = g.scale * 1.4426950408889634f;
+    p.tau = tau;
+    if (g.dtype == 1)
+        return s2o ? launch_d<__bf16, true>(p, stream) : launch_d<__bf16, false>(p, stream);
+    return s2o ? launch_d<float, true>(p, stream) : launch_d<float, false>(p, stream);
+}
+
+}  // namespace s2o

@@ -1,0 +1,177 @@
+// Importance estimator for gfx950: mean-pooled query per tile, fp32 key scores.
+//
+// "S2O: Early Stopping for Sparse Attention via Online Permutation",
+// gist.science technical summary, "Classement par Segment" (KV_perm): history
+// keys are scored against a representative query; a causal mask keeps only
+// prefix keys.  The representative is the mean of the tile's query rows.
+//
+// Scores are defined bit-exactly: qbar[k] = (fp32 sum of the BM rows in
+// ascending order) * (1/BM), then s[j] = fma chain over k = 0..d-1 starting
+// from 0.  The work is plain fp32 ALU (2*d flops per (tile, key) pair); the
+// fixed accumulation order rules out matrix cores.
+//
+// Layout of the score kernel: one workgroup per (b, KV head, segment s >= 1,
+// block of 256 history keys).  Each thread holds one key row in fp32
+// registers and runs it against every (query head of the group, tile of the
+// segment) pair, whose pooled queries are staged through LDS and read as
+// broadcasts.  Two pairs are kept in flight for instruction-level
+// parallelism; each chain is still evaluated in ascending k.
+#include "s2o_internal.h"
+
+namespace s2o {
+namespace {
+
+template <typename T>
+__device__ inline float widen(T x);
+template <>
+__device__ inline float widen<float>(float x) { return x; }
+template <>
+__device__ inline float widen<__bf16>(__bf16 x) {
+    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, x) << 16);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, float *__restrict__ qbar,
+                                                   Geometry g, int64_t total) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int k = (int)(gid % g.d);
+    const int64_t tile = gid / g.d;  // (b*Hq + h)*T + t
+    const int t = (int)(tile % g.T);
+    const int64_t bh = tile / g.T;
+    const T *src = Q + (bh * g.N + (int64_t)t * g.BM) * g.d + k;
+    float sum = 0.0f;
+    for (int r = 0; r < g.BM; ++r) sum = sum + widen<T>(src[(int64_t)r * g.d]);
+    qbar[gid] = sum * (1.0f / (float)g.BM);  // exact: BM is a power of two
+}
+
+constexpr int SCORE_KEYS = 256;   // keys per workgroup (one per thread)
+constexpr int SCORE_BATCH = 32;   // pooled queries staged in LDS at a time
+constexpr int SCORE_ILP = 2;      // pairs evaluated together (more spills the key row)
+
+template <typename T, int D>
+__global__ __launch_bounds__(SCORE_KEYS) void score_kernel(const float *__restrict__ qbar,
+                                                           const T *__restrict__ K,
+                                                           float *__restrict__ scores, Geometry g,
+                                                           int nseg) {
+    __shared__ __attribute__((aligned(16))) float qs[SCORE_BATCH][D];
+    const int s = blockIdx.y % nseg;             // segment of the query tiles
+    const int bg = blockIdx.y / nseg;            // b * Hkv + kv head
+    const int hist = s * g.S;                    // history length of the segment's tiles
+    const int j0 = blockIdx.x * SCORE_KEYS;
+    if (s == 0 || j0 >= hist) return;
+    const int b = bg / g.Hkv, kvh = bg % g.Hkv;
+    const int t_first = s * g.P;
+    const int t_end = min(g.T, (s + 1) * g.P);
+    const int ntiles = t_end - t_first;
+    const int npairs = ntiles * g.G;             // pair p -> (query head kvh*G + p / ntiles, tile)
+    const int j = j0 + (int)threadIdx.x;
+    const bool live = j < hist;
+
+    float kr[D];
+    {
+        const T *row = K + ((int64_t)bg * g.N + (live ? j : 0)) * D;
+#pragma unroll
+        for (int k = 0; k < D; k += 8) {
+            uint4 raw = *reinterpret_cast<const uint4 *>(row + k);  // 8 bf16 or 4 fp32
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    kr[k + 2 * e] = __uint_as_float(w[e] << 16);
+                    kr[k + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+                }
+            } else {
+                kr[k] = __uint_as_float(raw.x);
+                kr[k + 1] = __uint_as_float(raw.y);
+                kr[k + 2] = __uint_as_float(raw.z);
+                kr[k + 3] = __uint_as_float(raw.w);
+                uint4 raw2 = *reinterpret_cast<const uint4 *>(row + k + 4);
+                kr[k + 4] = __uint_as_float(raw2.x);
+                kr[k + 5] = __uint_as_float(raw2.y);
+                kr[k + 6] = __uint_as_float(raw2.z);
+                kr[k + 7] = __uint_as_float(raw2.w);
+            }
+        }
+    }
+
+    for (int p0 = 0; p0 < npairs; p0 += SCORE_BATCH) {
+        const int nb = min(SCORE_BATCH, npairs - p0);
+        __syncthreads();
+        for (int e = threadIdx.x; e < nb * D; e += SCORE_KEYS) {
+            int pp = p0 + e / D;
+            int h = kvh * g.G + pp / ntiles;
+            int t = t_first + pp % ntiles;
+            qs[e / D][e % D] = qbar[(((int64_t)b * g.Hq + h) * g.T + t) * D + e % D];
+        }
+        __syncthreads();
+        for (int q0 = 0; q0 < nb; q0 += SCORE_ILP) {
+            float acc[SCORE_ILP];
+#pragma unroll
+            for (int i = 0; i < SCORE_ILP; ++i) acc[i] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < D; k += 4) {
+#pragma unroll
+                for (int i = 0; i < SCORE_ILP; ++i) {
+                    const int qi = min(q0 + i, SCORE_BATCH - 1);
+                    float4 qv = *reinterpret_cast<const float4 *>(&qs[qi][k]);
+                    acc[i] = __builtin_fmaf(qv.x, kr[k], acc[i]);
+                    acc[i] = __builtin_fmaf(qv.y, kr[k + 1], acc[i]);
+                    acc[i] = __builtin_fmaf(qv.z, kr[k + 2], acc[i]);
+                    acc[i] = __builtin_fmaf(qv.w, kr[k + 3], acc[i]);
+                }
+            }
+            if (live) {
+#pragma unroll
+                for (int i = 0; i < SCORE_ILP; ++i) {
+                    if (q0 + i < nb) {
+                        int pp = p0 + q0 + i;
+                        int h = kvh * g.G + pp / ntiles;
+                        int t = t_first + pp % ntiles;
+                        scores[list_offset(g, b, h, t) + j] = acc[i];
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, hipStream_t stream) {
+    int64_t total = (int64_t)g.B * g.Hq * g.T * g.d;
+    unsigned blocks = (unsigned)((total + 255) / 256);
+    if (g.dtype == 1)
+        hipLaunchKernelGGL(pool_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const __bf16 *>(Q), qbar, g, total);
+    else
+        hipLaunchKernelGGL(pool_kernel<float>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const float *>(Q), qbar, g, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_score(const Geometry &g, const float *qbar, const void *K, float *scores,
+                        hipStream_t stream) {
+    const int nseg = (g.N + g.S - 1) / g.S;
+    if (nseg < 2) return hipSuccess;  // no tile has history
+    const int64_t max_hist = (int64_t)(nseg - 1) * g.S;
+    dim3 grid((unsigned)((max_hist + SCORE_KEYS - 1) / SCORE_KEYS), (unsigned)(g.B * g.Hkv * nseg));
+    if (g.dtype == 1) {
+        if (g.d == 128)
+            hipLaunchKernelGGL((score_kernel<__bf16, 128>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
+                               reinterpret_cast<const __bf16 *>(K), scores, g, nseg);
+        else
+            hipLaunchKernelGGL((score_kernel<__bf16, 64>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
+                               reinterpret_cast<const __bf16 *>(K), scores, g, nseg);
+    } else {
+        if (g.d == 128)
+            hipLaunchKernelGGL((score_kernel<float, 128>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
+                               reinterpret_cast<const float *>(K), scores, g, nseg);
+        else
+            hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
+                               reinterpret_cast<const float *>(K), scores, g, nseg);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace s2o

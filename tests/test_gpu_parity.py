@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small problems are compared on every tile, spanning several tiles, segments
+and a ragged last segment; the Llama-3.1-8B-shaped 16K/128K workloads are
+compared on sampled tiles at their full size, in the launch configuration the
+benchmark times.  Acceptance rules are in parity_util.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_prefill_amd as s2o
+import oracle
+from long_context_prefill_amd import synth
+from parity_util import GpuRun, assert_report, compare, f64, sample_tiles, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def all_tiles(w):
+    return [(b, h, t) for b in range(w.B) for h in range(w.Hq) for t in range(w.N // w.tile_m)]
+
+
+# ------------------------------------------------------------------ fp32 ---
+
+def test_tiny_f32_single_segment_is_dense():
+    """N = S = 2048, d = 64, fp32: one segment, so the method is pass 1 only."""
+    w = synth.WORKLOADS["tiny_f32_n2048"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    assert s2o.list_entries(run.p) == 0
+    o, ex = run.attn(w.taus[0])
+    rep = compare(run, all_tiles(w), w.taus[0], o, ex)
+    assert_report(rep, "f32")
+    od = run.dense()
+    ref = oracle.dense_rows(run.po, x["q"], x["k"], x["v"], 0, 0, 0, w.N)
+    assert np.abs(f64(od[0, 0]) - ref).max() <= 1e-4
+
+
+@pytest.mark.parametrize("tau", [1e-3, 0.0, 3e-2])
+def test_tiny_f32_segments_512(tau):
+    """Same inputs with 512-token segments: lists, early stop and outputs (max-abs 1e-4)."""
+    w = synth.WORKLOADS["tiny_f32_n2048_s512"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    o, ex = run.attn(tau)
+    rep = compare(run, all_tiles(w), tau, o, ex)
+    assert_report(rep, "f32")
+
+
+# ------------------------------------------------------- small bf16, every tile --
+
+SMALL = [
+    # name, B, Hq, Hkv, N, d, BM, S, structure
+    ("gqa_ragged_d128_bm128", 2, 4, 2, 1024, 128, 128, 384, "stripes+band"),
+    ("d64_bm64", 1, 2, 1, 768, 64, 64, 192, "stripes"),
+    ("d64_bm128", 1, 2, 2, 1024, 64, 128, 256, "stripes"),
+    ("d128_bm64", 1, 4, 1, 640, 128, 64, 128, "stripes+band"),
+    ("uniform_d128", 1, 2, 1, 1024, 128, 128, 256, "uniform"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_bf16_every_tile(case):
+    name, B, Hq, Hkv, N, d, BM, S, structure = case
+    w = synth.custom_workload(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", tile_m=BM, tile_n=64,
+                              seg_len=S, structure=structure, n_stripes=max(N // 100, 4),
+                              seed=500 + N + d, name=name)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    for tau in (0.0, 1e-3, 3e-2, 0.3):
+        o, ex = run.attn(tau)
+        rep = compare(run, all_tiles(w), tau, o, ex, check_lists=False)
+        assert_report(rep, "bf16")
+
+
+def test_dense_kernel_matches_oracle_bf16():
+    w = synth.custom_workload(B=1, Hq=4, Hkv=2, N=1024, d=128, dtype="bf16", tile_m=128,
+                              seg_len=1024, structure="stripes+band", n_stripes=10, seed=77)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    od = f64(run.dense())
+    reqs = [(0, h, 0, 1024) for h in range(4)]
+    refs = oracle.dense_requests(run.po, x["q"], x["k"], x["v"], reqs)
+    for h in range(4):
+        d = np.abs(od[0, h] - refs[h])
+        assert d.max() <= 2e-2 and d.mean() <= 2e-3, (h, d.max(), d.mean())
+
+
+def test_dense_non_causal_bf16():
+    """causal = 0 (dense kernel only): every row attends to every key."""
+    w = synth.custom_workload(B=1, Hq=2, Hkv=1, N=512, d=128, dtype="bf16", tile_m=128,
+                              seg_len=512, structure="stripes", n_stripes=5, seed=78)
+    x = synth.make_inputs(w)
+    q, k, v = (to_device(x[n]) for n in ("q", "k", "v"))
+    p = s2o.problem(1, 2, 1, 512, 128, 1, 512, 128, 64, causal=False)
+    say("dense non-causal")
+    od = f64(s2o.dense_attn_fwd(p, q, k, v))
+    qf = synth.f32_from_bf16_bits(x["q"]).astype(np.float64)
+    kf = synth.f32_from_bf16_bits(x["k"]).astype(np.float64)
+    vf = synth.f32_from_bf16_bits(x["v"]).astype(np.float64)
+    for h in range(2):
+        s = (qf[0, h] @ kf[0, 0].T) / np.sqrt(128)
+        pr = np.exp(s - s.max(axis=1, keepdims=True))
+        ref = (pr / pr.sum(axis=1, keepdims=True)) @ vf[0, 0]
+        d = np.abs(od[0, h] - ref)
+        assert d.max() <= 2e-2 and d.mean() <= 2e-3
+
+
+# --------------------------------------------------------------- closed form --
+
+def test_q_zero_closed_form_on_gpu():
+    """Q = 0: all logits and scores are 0, lists ascend, and the executed-tile count of
+    every tile follows the closed form (first row has the largest gain)."""
+    N, d, BM, BN, S, tau = 2048, 128, 128, 64, 256, 0.02
+    rng = np.random.default_rng(5)
+    q = np.zeros((1, 1, N, d), dtype=np.uint16)
+    k = synth.bf16_bits_from_f32(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    v = synth.bf16_bits_from_f32(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    p = s2o.problem(1, 1, 1, N, d, 1, S, BM, BN)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    say("q=0 closed form")
+    sc = s2o.s2o_score(p, qd, kd)
+    idx = s2o.s2o_build_index(p, sc)
+    o, ex = s2o.s2o_attn_fwd(p, qd, kd, vd, idx, tau)
+    torch.cuda.synchronize()
+    ex = ex.cpu().numpy()[0, 0]
+    og = f64(o)[0, 0]
+    vf = synth.f32_from_bf16_bits(v).astype(np.float64)[0, 0]
+    for t in range(N // BM):
+        a = (t * BM // S) * S
+        assert np.array_equal(idx[s2o.list_offset(p, 0, 0, t):][:a].cpu().numpy(), np.arange(a))
+        C, r0, n = a // BN, t * BM - a, a // BN
+        for c in range(C):
+            if BN < tau * (r0 + 1 + BN * (c + 1)):
+                n = c + 1
+                break
+        assert ex[t] == ((t + 1) * BM - a) // BN + n, t
+        for r in (0, 63, 127):
+            i = t * BM + r
+            keys = list(range(a, i + 1)) + list(range(n * BN))
+            assert np.abs(og[i] - vf[keys].mean(axis=0)).max() <= 2e-2
+
+
+# ------------------------------------------------- Llama-3.1-8B shape, full size --
+
+@pytest.fixture(scope="module")
+def llama16k():
+    w = synth.WORKLOADS["llama8b_n16k"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    yield run
+    del run
+    torch.cuda.empty_cache()
+
+
+def test_llama8b_16k_scores_and_lists_bit_exact(llama16k):
+    run = llama16k
+    say("oracle scores + lists for all 16K tiles")
+    scores_o = oracle.scores_all(run.po, run.x["q"], run.x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+
+
+@pytest.mark.parametrize("tau", [1e-2, 1e-3, 1e-4])
+def test_llama8b_16k_sampled(llama16k, tau):
+    run = llama16k
+    tiles = sample_tiles(run.w, heads=(0, 9, 18, 27), n_random=16, seed=1)
+    o, ex = run.attn(tau)
+    rep = compare(run, tiles, tau, o, ex, check_lists=False)
+    assert_report(rep, "bf16")
+
+
+def test_llama8b_16k_tau0_equals_dense(llama16k):
+    run = llama16k
+    o, ex = run.attn(0.0)
+    od = run.dense()
+    d = (o.float() - od.float()).abs()
+    say(f"tau=0 vs dense: max {d.max().item():.3e} mean {d.mean().item():.3e}")
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+    T = run.w.N // run.w.tile_m
+    want = torch.tensor([((t + 1) * 128) // 64 for t in range(T)], dtype=torch.int32)
+    assert torch.equal(ex.cpu()[0], want.expand(run.w.Hq, T))
+
+
+def test_llama8b_16k_deterministic(llama16k):
+    run = llama16k
+    s2 = s2o.s2o_score(run.p, run.q, run.k)
+    i2 = s2o.s2o_build_index(run.p, s2)
+    o1, e1 = run.attn(1e-3)
+    o2, e2 = s2o.s2o_attn_fwd(run.p, run.q, run.k, run.v, i2, 1e-3)
+    torch.cuda.synchronize()
+    assert torch.equal(s2.view(torch.int32), run.scores.view(torch.int32))
+    assert torch.equal(i2, run.idx)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(e1, e2)
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_128k_sampled():
+    """The headline shape: N = 131072, 32 Q / 8 KV heads, d = 128, bf16, S = 8192."""
+    w = synth.WORKLOADS["llama8b_n128k"]
+    say("generating llama8b_n128k inputs")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    tiles = sample_tiles(w, heads=(0, 27), n_random=8, seed=3)
+    for tau in (1e-3, 1e-2):
+        o, ex = run.attn(tau)
+        say(f"oracle on {len(tiles)} sampled tiles")
+        rep = compare(run, tiles, tau, o, ex, check_lists=(tau == 1e-3))
+        assert_report(rep, "bf16")
+        del o, ex
+
+
+@pytest.mark.timeout(900)
+def test_uniform_128k_tau0_and_overhead_case():
+    """No planted structure: tau = 0 must equal the dense kernel; tau = 1e-3 on samples."""
+    w = synth.WORKLOADS["uniform_n128k"]
+    say("generating uniform_n128k inputs")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    o0, ex0 = run.attn(0.0)
+    od = run.dense()
+    d = (o0.float() - od.float()).abs()
+    say(f"tau=0 vs dense: max {d.max().item():.3e} mean {d.mean().item():.3e}")
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+    del o0, od, d
+    tiles = sample_tiles(w, heads=(5,), n_random=6, seed=4)
+    o, ex = run.attn(1e-3)
+    rep = compare(run, tiles, 1e-3, o, ex, check_lists=True)
+    assert_report(rep, "bf16")
+
+
+# ----------------------------------------------------------------- edge cases --
+
+def test_no_history_when_segment_covers_sequence():
+    w = synth.custom_workload(B=1, Hq=2, Hkv=1, N=512, d=128, dtype="bf16", tile_m=128,
+                              seg_len=1024, structure="stripes", n_stripes=5, seed=79)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    assert run.scores.numel() == 0 and run.idx.numel() == 0
+    o, ex = run.attn(1e-3)
+    assert_report(compare(run, all_tiles(w), 1e-3, o, ex), "bf16")
+
+
+def test_single_tile_sequence():
+    w = synth.custom_workload(B=1, Hq=1, Hkv=1, N=128, d=128, dtype="bf16", tile_m=128,
+                              seg_len=128, structure="stripes", n_stripes=2, seed=80)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    o, ex = run.attn(0.5)
+    assert_report(compare(run, all_tiles(w), 0.5, o, ex), "bf16")
+
+
+def test_errors_raise_on_gpu():
+    p = s2o.problem(1, 1, 1, 256, 128, 1, 128, 128, 64)
+    q = torch.zeros(1, 1, 256, 128, dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros(s2o.list_entries(p), dtype=torch.int32, device="cuda")
+    with pytest.raises(s2o.S2OError):
+        s2o.s2o_attn_fwd(p, q, q, q, idx, -1.0)
+    with pytest.raises(ValueError):
+        s2o.s2o_attn_fwd(p, q.float(), q, q, idx, 0.0)

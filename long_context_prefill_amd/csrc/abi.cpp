@@ -2,7 +2,7 @@
 // contract of every function is documented in include/s2o.h.
 #include <math.h>
 
-#include "../../include/s2o.h"
+#include "s2o.h"
 #include "s2o_internal.h"
 
 namespace {

@@ -13,9 +13,10 @@
 // Layout of the score kernel: one workgroup per (b, KV head, segment s >= 1,
 // block of 256 history keys).  Each thread holds one key row in fp32
 // registers and runs it against every (query head of the group, tile of the
-// segment) pair, whose pooled queries are staged through LDS and read as
-// broadcasts.  Two pairs are kept in flight for instruction-level
-// parallelism; each chain is still evaluated in ascending k.
+// segment) pair.  A pair's pooled query is the same for the whole wave, so it
+// is read through the scalar cache and fed to the fmas as SGPR operands (no
+// VGPRs, which keeps three waves per SIMD).  Two pairs are kept in flight for
+// instruction-level parallelism; each chain is still evaluated in ascending k.
 #include "s2o_internal.h"
 
 namespace s2o {
@@ -46,15 +47,13 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, floa
 }
 
 constexpr int SCORE_KEYS = 256;   // keys per workgroup (one per thread)
-constexpr int SCORE_BATCH = 32;   // pooled queries staged in LDS at a time
-constexpr int SCORE_ILP = 2;      // pairs evaluated together (more spills the key row)
+constexpr int SCORE_ILP = 2;      // pairs evaluated together (independent fma chains)
 
 template <typename T, int D>
-__global__ __launch_bounds__(SCORE_KEYS) void score_kernel(const float *__restrict__ qbar,
-                                                           const T *__restrict__ K,
-                                                           float *__restrict__ scores, Geometry g,
-                                                           int nseg) {
-    __shared__ __attribute__((aligned(16))) float qs[SCORE_BATCH][D];
+__global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__restrict__ qbar,
+                                                              const T *__restrict__ K,
+                                                              float *__restrict__ scores,
+                                                              Geometry g, int nseg) {
     const int s = blockIdx.y % nseg;             // segment of the query tiles
     const int bg = blockIdx.y / nseg;            // b * Hkv + kv head
     const int hist = s * g.S;                    // history length of the segment's tiles
@@ -62,8 +61,7 @@ __global__ __launch_bounds__(SCORE_KEYS) void score_kernel(const float *__restri
     if (s == 0 || j0 >= hist) return;
     const int b = bg / g.Hkv, kvh = bg % g.Hkv;
     const int t_first = s * g.P;
-    const int t_end = min(g.T, (s + 1) * g.P);
-    const int ntiles = t_end - t_first;
+    const int ntiles = min(g.T, (s + 1) * g.P) - t_first;
     const int npairs = ntiles * g.G;             // pair p -> (query head kvh*G + p / ntiles, tile)
     const int j = j0 + (int)threadIdx.x;
     const bool live = j < hist;
@@ -82,11 +80,11 @@ __global__ __launch_bounds__(SCORE_KEYS) void score_kernel(const float *__restri
                     kr[k + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
                 }
             } else {
+                uint4 raw2 = *reinterpret_cast<const uint4 *>(row + k + 4);
                 kr[k] = __uint_as_float(raw.x);
                 kr[k + 1] = __uint_as_float(raw.y);
                 kr[k + 2] = __uint_as_float(raw.z);
                 kr[k + 3] = __uint_as_float(raw.w);
-                uint4 raw2 = *reinterpret_cast<const uint4 *>(row + k + 4);
                 kr[k + 4] = __uint_as_float(raw2.x);
                 kr[k + 5] = __uint_as_float(raw2.y);
                 kr[k + 6] = __uint_as_float(raw2.z);
@@ -95,42 +93,32 @@ __global__ __launch_bounds__(SCORE_KEYS) void score_kernel(const float *__restri
         }
     }
 
-    for (int p0 = 0; p0 < npairs; p0 += SCORE_BATCH) {
-        const int nb = min(SCORE_BATCH, npairs - p0);
-        __syncthreads();
-        for (int e = threadIdx.x; e < nb * D; e += SCORE_KEYS) {
-            int pp = p0 + e / D;
-            int h = kvh * g.G + pp / ntiles;
-            int t = t_first + pp % ntiles;
-            qs[e / D][e % D] = qbar[(((int64_t)b * g.Hq + h) * g.T + t) * D + e % D];
+    // pooled queries are wave-uniform: read them through the scalar cache so the
+    // fma chains take them as SGPR operands
+    for (int p0 = 0; p0 < npairs; p0 += SCORE_ILP) {
+        const float *qp[SCORE_ILP];
+#pragma unroll
+        for (int i = 0; i < SCORE_ILP; ++i) {
+            const int pp = min(p0 + i, npairs - 1);
+            const int hq = pp / ntiles;
+            const int t = t_first + pp - hq * ntiles;
+            qp[i] = qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.T + t) * D;
         }
-        __syncthreads();
-        for (int q0 = 0; q0 < nb; q0 += SCORE_ILP) {
-            float acc[SCORE_ILP];
+        float acc[SCORE_ILP];
 #pragma unroll
-            for (int i = 0; i < SCORE_ILP; ++i) acc[i] = 0.0f;
+        for (int i = 0; i < SCORE_ILP; ++i) acc[i] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < D; k += 4) {
+        for (int k = 0; k < D; ++k) {
 #pragma unroll
-                for (int i = 0; i < SCORE_ILP; ++i) {
-                    const int qi = min(q0 + i, SCORE_BATCH - 1);
-                    float4 qv = *reinterpret_cast<const float4 *>(&qs[qi][k]);
-                    acc[i] = __builtin_fmaf(qv.x, kr[k], acc[i]);
-                    acc[i] = __builtin_fmaf(qv.y, kr[k + 1], acc[i]);
-                    acc[i] = __builtin_fmaf(qv.z, kr[k + 2], acc[i]);
-                    acc[i] = __builtin_fmaf(qv.w, kr[k + 3], acc[i]);
-                }
-            }
-            if (live) {
+            for (int i = 0; i < SCORE_ILP; ++i) acc[i] = __builtin_fmaf(qp[i][k], kr[k], acc[i]);
+        }
 #pragma unroll
-                for (int i = 0; i < SCORE_ILP; ++i) {
-                    if (q0 + i < nb) {
-                        int pp = p0 + q0 + i;
-                        int h = kvh * g.G + pp / ntiles;
-                        int t = t_first + pp % ntiles;
-                        scores[list_offset(g, b, h, t) + j] = acc[i];
-                    }
-                }
+        for (int i = 0; i < SCORE_ILP; ++i) {
+            const int pp = p0 + i;
+            if (live && pp < npairs) {
+                const int hq = pp / ntiles;
+                const int t = t_first + pp - hq * ntiles;
+                scores[list_offset(g, b, kvh * g.G + hq, t) + j] = acc[i];
             }
         }
     }

@@ -50,8 +50,11 @@ struct AttnParams {
     float tau;
 };
 
-// Block -> (b, h, t).  Units (b, kv head, t) are ordered t-descending; the G
-// query heads of a unit get block ids congruent mod 8, i.e. the same XCD.
+// Block -> (b, h, t).  Units (kv head, t, b) are ordered KV-head-major and,
+// within a KV head, t-descending (heaviest tiles first), so that at any time
+// the whole chip gathers from one KV head's K/V (67 MB at 128K), which stays in
+// the Infinity Cache.  The G query heads of a unit get block ids congruent
+// mod 8, i.e. the same XCD, where they share its L2.
 struct Work {
     int b, h, t;
 };
@@ -63,11 +66,12 @@ __device__ inline bool map_block(const Geometry &g, Work &w) {
     int u = 8 * (r / g.G) + x;
     int units = g.B * g.Hkv * g.T;
     if (u >= units) return false;
-    int per_t = g.B * g.Hkv;
-    w.t = g.T - 1 - u / per_t;
-    int rem = u % per_t;
-    w.b = rem / g.Hkv;
-    w.h = (rem % g.Hkv) * g.G + hq;
+    int per_g = g.T * g.B;
+    int kvh = u / per_g;
+    int rem = u % per_g;
+    w.t = g.T - 1 - rem / g.B;
+    w.b = rem % g.B;
+    w.h = kvh * g.G + hq;
     return true;
 }
 
@@ -92,19 +96,24 @@ __device__ inline void mask_chunk(f32x16 &s0, f32x16 &s1, int key0, int row, int
 }
 
 // Online-softmax update of one chunk for this lane's row.  Turns s0/s1 into
-// probabilities exp2(s*c - m_new); returns the chunk mass delta (against
-// m_new) and the rescale factor of the old state.
+// probabilities exp2(s*c - m); returns the chunk mass delta and the rescale
+// factor of the old state.  The running max m is only moved when the chunk's
+// max exceeds it by more than kMaxSlack (log2 units): probabilities then stay
+// below 2^kMaxSlack, and since l, delta and acc all use the same m the result
+// (acc / l, delta / l) is unchanged while most chunks skip the rescale.
+constexpr float kMaxSlack = 8.0f;
+
 __device__ inline void softmax_chunk(f32x16 &s0, f32x16 &s1, float c, float &m, float &l,
                                      float &alpha, float &delta) {
     float mx = fmaxf(max16(s0), max16(s1));
-    mx = fmaxf(mx, partner(mx));
-    float m_new = fmaxf(m, mx * c);
-    alpha = exp2f(m - m_new);  // 0 on the first chunk (m = -inf)
+    mx = fmaxf(mx, partner(mx)) * c;
+    float m_new = mx > m + kMaxSlack ? mx : m;
+    alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first chunk (m = -inf)
     float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        s0[r] = exp2f(fmaf(s0[r], c, -m_new));
-        s1[r] = exp2f(fmaf(s1[r], c, -m_new));
+        s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
+        s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += s0[r] + s1[r];
@@ -116,8 +125,7 @@ __device__ inline void softmax_chunk(f32x16 &s0, f32x16 &s1, float c, float &m, 
 
 template <int NACC>
 __device__ inline void rescale(f32x16 (&acc)[NACC], float alpha) {
-    // skip when no row of the wave changed its max (common once the list's
-    // largest keys have been seen)
+    // skip when no row of the wave moved its max
     if (__ballot(alpha != 1.0f) == 0) return;
 #pragma unroll
     for (int i = 0; i < NACC; ++i)

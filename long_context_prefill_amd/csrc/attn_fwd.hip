@@ -75,7 +75,18 @@ __device__ inline bool map_block(const Geometry &g, Work &w) {
     return true;
 }
 
-__device__ inline float partner(float x) { return __shfl_xor(x, 32); }
+// Lanes l and l^32 hold the two halves of one query row.  v_permlane32_swap
+// applied to (x, x) leaves x of lane l and of lane l^32 in the two results (in
+// the same order in both lanes), so max/sum of the pair are bit-identical in
+// the two lanes.
+__device__ inline float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float max16(const f32x16 &v) {
     float m = v[0];
@@ -105,8 +116,7 @@ constexpr float kMaxSlack = 8.0f;
 
 __device__ inline void softmax_chunk(f32x16 &s0, f32x16 &s1, float c, float &m, float &l,
                                      float &alpha, float &delta) {
-    float mx = fmaxf(max16(s0), max16(s1));
-    mx = fmaxf(mx, partner(mx)) * c;
+    float mx = pair_max(fmaxf(max16(s0), max16(s1))) * c;
     float m_new = mx > m + kMaxSlack ? mx : m;
     alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first chunk (m = -inf)
     float sum = 0.f;
@@ -117,7 +127,7 @@ __device__ inline void softmax_chunk(f32x16 &s0, f32x16 &s1, float c, float &m, 
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) sum += s0[r] + s1[r];
-    sum += partner(sum);
+    sum = pair_sum(sum);
     delta = sum;
     l = l * alpha + sum;
     m = m_new;
@@ -168,7 +178,7 @@ struct Cfg {
 };
 
 template <typename T, int D, int NW, bool S2O>
-__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel(AttnParams a) {
+__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel_staged(AttnParams a) {
     using C = Cfg<T, D, NW, S2O>;
     constexpr int BM = C::BM, NT = C::NT, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -183,7 +193,6 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
     const int li = lane & 31, half = lane >> 5;
     const int row0 = t * BM;
     const int my_row = row0 + 32 * wave + li;
-    const int wave_last_row = row0 + 32 * wave + 31;
 
     // schedule: pass-1 chunks are contiguous key tiles starting at base1; pass-2
     // chunks are consecutive BN-entry slices of the tile's list
@@ -301,91 +310,180 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
     float m = -INFINITY, l = 0.f;
     const float c = a.scale_log2;
 
-    // prologue: chunk 0 -> LDS stage 0, rows of chunk 1 in registers
+    // QK^T of the chunk in stage `buf`: s0/s1 = keys 0..31 / 32..63 of the
+    // chunk against this lane's query row
+    auto qk = [&](int buf, f32x16 &s0, f32x16 &s1) {
+        const T *Kl = lds + buf * C::BUF;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+        if constexpr (C::kBf16) {
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) {
+                bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 16 * s + 8 * half);
+                bf16x8 kb = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 16 * s + 8 * half);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s], s1, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < D / 2; ++s) {
+                float ka = Kl[li * C::KSTR + 2 * s + half];
+                float kb = Kl[(32 + li) * C::KSTR + 2 * s + half];
+                s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kb, qf[s], s1, 0, 0, 0);
+            }
+        }
+    };
+    // O^T += V^T P^T with the probabilities of the chunk in stage `buf`
+    auto pv = [&](int buf, const f32x16 &p0, const f32x16 &p1) {
+        const T *Vl = lds + buf * C::BUF + C::KBUF;
+        if constexpr (C::kBf16) {
+            bf16x8 pb[4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[0][e] = (__bf16)p0[e];
+                pb[1][e] = (__bf16)p0[8 + e];
+                pb[2][e] = (__bf16)p1[e];
+                pb[3][e] = (__bf16)p1[8 + e];
+            }
+            const uint16_t *Vt = reinterpret_cast<const uint16_t *>(Vl);
+#pragma unroll
+            for (int cb = 0; cb < NACC; ++cb) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const uint16_t *src = Vt + (32 * cb + li) * C::VSTR + 16 * s + 8 * half;
+                    u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
+                    u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 4);
+                    bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < NACC; ++cb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    int j = 8 * (r >> 2) + 4 * half + (r & 3);
+                    float v0 = Vl[j * C::VSTR + 32 * cb + li];
+                    float v1 = Vl[(32 + j) * C::VSTR + 32 * cb + li];
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, p0[r], acc[cb], 0, 0, 0);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, p1[r], acc[cb], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Software pipeline.  During iteration k the LDS stages hold chunks k and
+    // k+1 and the registers receive chunk k+2; the matrix cores compute
+    // S_{k+1} = K_{k+1} Q^T while the vector ALUs run the softmax of chunk k,
+    // then PV(k) accumulates.  After a stop the speculative S_{k+1} is dropped.
     fetch_rows(0);
     issue_loads();
-    if (total > 1) fetch_rows(1);
     store_lds(0);
+    if (total > 1) {
+        fetch_rows(1);
+        issue_loads();
+        store_lds(1);
+    }
+    if (total > 2) fetch_rows(2);
     __syncthreads();
+    f32x16 s0, s1;
+    qk(0, s0, s1);
 
     int executed2 = 0;
     for (int k = 0; k < total; ++k) {
         const int buf = k & 1;
-        const bool has_next = k + 1 < total;
-        if (has_next) {
+        const bool has2 = k + 2 < total;
+        if (has2) {
             issue_loads();
-            if (k + 2 < total) fetch_rows(k + 2);
+            if (k + 3 < total) fetch_rows(k + 3);
         }
-        const T *Kl = lds + buf * C::BUF;
-        const T *Vl = Kl + C::KBUF;
         const bool is_p2 = S2O && k >= n1;
         const int key0 = is_p2 ? 0 : base1 + k * BN;
-        bool wave_cont = false;
-        // a wave whose rows all precede the chunk has nothing to add
-        const bool skip = !is_p2 && g.causal && key0 > wave_last_row;
-        if (!skip) {
-            f32x16 s0, s1;
+        if (!is_p2 && g.causal && key0 + BN - 1 > row0 + 32 * wave) mask_chunk(s0, s1, key0, my_row, half);
+
+        // row max of chunk k and the (lazy) new running max
+        const float mx = pair_max(fmaxf(max16(s0), max16(s1))) * c;
+        const float m_new = mx > m + kMaxSlack ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+
+        // phase 1: S_{k+1} = K_{k+1} Q^T on the matrix cores, interleaved with
+        // the exponentials of chunk k (stale data when k+1 == total; unused then)
+        f32x16 sn0, sn1;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-            if constexpr (C::kBf16) {
+        for (int r = 0; r < 16; ++r) sn0[r] = sn1[r] = 0.f;
+        if constexpr (C::kBf16) {
+            const T *Kl = lds + (buf ^ 1) * C::BUF;
+            constexpr int STEPS = D / 16;
+            constexpr int EPS = 16 / STEPS;  // exponentials per block per step
+            bf16x8 ka[2], kb[2];
+            ka[0] = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 8 * half);
+            kb[0] = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 8 * half);
 #pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
-                    bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 16 * s + 8 * half);
-                    bf16x8 kb = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 16 * s + 8 * half);
-                    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s], s1, 0, 0, 0);
+            for (int st = 0; st < STEPS; ++st) {
+                if (st + 1 < STEPS) {
+                    ka[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 16 * (st + 1) + 8 * half);
+                    kb[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 16 * (st + 1) + 8 * half);
                 }
-            } else {
+                sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1], qf[st], sn0, 0, 0, 0);
+                sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[st & 1], qf[st], sn1, 0, 0, 0);
 #pragma unroll
-                for (int s = 0; s < D / 2; ++s) {
-                    float ka = Kl[li * C::KSTR + 2 * s + half];
-                    float kb = Kl[(32 + li) * C::KSTR + 2 * s + half];
-                    s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[s], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kb, qf[s], s1, 0, 0, 0);
+                for (int e = 0; e < EPS; ++e) {
+                    const int r = st * EPS + e;
+                    s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
+                    s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (!is_p2 && g.causal && key0 + BN - 1 > row0 + 32 * wave) mask_chunk(s0, s1, key0, my_row, half);
-            float alpha, delta;
-            softmax_chunk(s0, s1, c, m, l, alpha, delta);
-            if (is_p2) wave_cont = __ballot(!(delta < a.tau * l)) != 0;
-            rescale(acc, alpha);
-            // O^T += V^T P^T
-            if constexpr (C::kBf16) {
-                bf16x8 pb[4];
+        } else {
+            qk(buf ^ 1, sn0, sn1);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pb[0][e] = (__bf16)s0[e];
-                    pb[1][e] = (__bf16)s0[8 + e];
-                    pb[2][e] = (__bf16)s1[e];
-                    pb[3][e] = (__bf16)s1[8 + e];
-                }
-                const uint16_t *Vt = reinterpret_cast<const uint16_t *>(Vl);
-#pragma unroll
-                for (int cb = 0; cb < NACC; ++cb) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        const uint16_t *src = Vt + (32 * cb + li) * C::VSTR + 16 * s + 8 * half;
-                        u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
-                        u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 4);
-                        bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int cb = 0; cb < NACC; ++cb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        int j = 8 * (r >> 2) + 4 * half + (r & 3);
-                        float v0 = Vl[j * C::VSTR + 32 * cb + li];
-                        float v1 = Vl[(32 + j) * C::VSTR + 32 * cb + li];
-                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, s0[r], acc[cb], 0, 0, 0);
-                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, s1[r], acc[cb], 0, 0, 0);
-                    }
-                }
+            for (int r = 0; r < 16; ++r) {
+                s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
+                s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
             }
         }
-        if (has_next) store_lds(buf ^ 1);
+        rescale(acc, alpha);
+
+        // phase 2: O^T += V^T P^T for chunk k, interleaved with the row sum
+        float sum = 0.f;
+        if constexpr (C::kBf16) {
+            const uint16_t *Vt = reinterpret_cast<const uint16_t *>(lds + buf * C::BUF + C::KBUF);
+            bf16x8 pb[4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[0][e] = (__bf16)s0[e];
+                pb[1][e] = (__bf16)s0[8 + e];
+                pb[2][e] = (__bf16)s1[e];
+                pb[3][e] = (__bf16)s1[8 + e];
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int cb = 0; cb < NACC; ++cb) {
+                    const uint16_t *src = Vt + (32 * cb + li) * C::VSTR + 16 * s + 8 * half;
+                    u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
+                    u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 4);
+                    bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
+                }
+                // 8 of the 32 probabilities of this lane per step
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum += s0[4 * s + e] + s1[4 * s + e];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            pv(buf, s0, s1);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += s0[r] + s1[r];
+        }
+        const float delta = pair_sum(sum);
+        l = l * alpha + delta;
+        const bool wave_cont = is_p2 && __ballot(!(delta < a.tau * l)) != 0;
+
+        __syncthreads();  // every wave is done with stage `buf` (K_k was read last iteration)
+        if (has2) store_lds(buf);
         if (is_p2 && lane == 0) flags[buf][wave] = wave_cont ? 1 : 0;
         __syncthreads();
         if (is_p2) {
@@ -395,6 +493,8 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
             for (int w = 0; w < NW; ++w) any |= flags[buf][w];
             if (!any) break;
         }
+        s0 = sn0;
+        s1 = sn1;
     }
 
     // epilogue: O = acc / l; lane holds O[my_row][32cb + 8q + 4half + 0..3]
@@ -421,20 +521,291 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
     if (a.exec && tid == 0) a.exec[((int64_t)b * g.Hq + h) * g.T + t] = n1 + executed2;
 }
 
-template <typename T, int D, int NW, bool S2O>
-hipError_t launch_one(const AttnParams &p, hipStream_t stream) {
-    using C = Cfg<T, D, NW, S2O>;
+// ---------------------------------------------------------------------------
+// bf16 kernel: K/V tiles move global -> LDS directly (global_load_lds_dwordx4,
+// one 16-byte row piece per lane, row-gathered through the chunk's indices),
+// so no VGPRs stage them and no VALU touches them on the way.  A tile is 64
+// rows of D bf16, row-major, its 16-byte pieces XOR-swizzled per row so that
+// the MFMA operand reads are free of bank conflicts:
+//   K: piece c of row r lives in slot c ^ kswz(r); the QK^T A operand is one
+//      16-byte read per lane;
+//   V: piece c of key j lives in slot c ^ vswz(j); the PV A operand (V^T) is
+//      read with ds_read_b64_tr_b16, which hands each lane four keys of one
+//      column: within a group of 16 lanes, lane i supplies the 8-byte read of
+//      (key e = i/4, columns 4*(i%4)..+3) and lane j receives column j of the
+//      four keys.
+// K runs one chunk ahead of V (QK^T of chunk k+1 overlaps the softmax of chunk
+// k), with two LDS stages each: iteration k issues K_{k+2} and V_{k+1} into
+// the stages freed by the previous iteration, and waits for them only at its
+// end, so every load has a whole iteration to land; one barrier per iteration.
+template <int D, int NW, bool S2O>
+struct BCfg {
+    static constexpr int BM = 32 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BN = kTileN;
+    static constexpr int CPR = D / 8;                  // 16-byte pieces per row
+    static constexpr int ROWB = D * 2;                 // bytes per row
+    static constexpr int TILEB = BN * ROWB;            // bytes per K or V tile
+    static constexpr int INSTR = BN * CPR / 64 / NW;   // piece loads per lane per tile
+    static constexpr size_t LDS_BYTES = 4 * TILEB;     // K stage 0/1, V stage 0/1
+    static_assert(INSTR >= 1, "tile too small for the thread count");
+};
+
+template <int D>
+__device__ inline int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ inline int vswz(int j) { return D == 128 ? ((j & 3) << 2) : (((j >> 1) & 1) << 2); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int D, int NW, bool S2O>
+__global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
+    using C = BCfg<D, NW, S2O>;
+    constexpr int BM = C::BM, BN = C::BN;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    unsigned char *lds = smem_raw;
+    __shared__ int flags[2][NW];
+
+    const Geometry &g = a.g;
+    Work wk;
+    if (!map_block(g, wk)) return;
+    const int b = wk.b, h = wk.h, t = wk.t;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int li = lane & 31, half = lane >> 5;
+    const int row0 = t * BM;
+    const int my_row = row0 + 32 * wave + li;
+
+    const int seg_a = S2O ? (int)seg_start(g, t) : 0;
+    const int base1 = seg_a;
+    const int n1 = g.causal ? (row0 + BM - base1) / BN : g.N / BN;
+    const int n2 = S2O ? seg_a / BN : 0;
+    const int total = n1 + n2;
+    const int32_t *list = S2O ? a.idx + list_offset(g, b, h, t) : nullptr;
+
+    const int kvh = h / g.G;
+    const __bf16 *Qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)(b * g.Hq + h) * g.N) * D;
+    const __bf16 *Kp = reinterpret_cast<const __bf16 *>(a.k) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
+    const __bf16 *Vp = reinterpret_cast<const __bf16 *>(a.v) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
+
+    auto chunk_row = [&](int k, int p) -> int {
+        return k < n1 ? base1 + k * BN + p : list[(k - n1) * BN + p];
+    };
+    // slot q = (wave*INSTR + i)*64 + lane of a tile: row q / CPR, slot q % CPR
+    auto slot_row = [&](int i) { return ((wave * C::INSTR + i) * 64 + lane) / C::CPR; };
+    auto slot_col = [&](int i) { return ((wave * C::INSTR + i) * 64 + lane) % C::CPR; };
+    int krows[C::INSTR], vrows[C::INSTR];
+    auto fetch_rows = [&](int k, int (&rows)[C::INSTR]) {
+#pragma unroll
+        for (int i = 0; i < C::INSTR; ++i) rows[i] = chunk_row(k, slot_row(i));
+    };
+    auto issue_k = [&](int stage, const int (&rows)[C::INSTR]) {
+#pragma unroll
+        for (int i = 0; i < C::INSTR; ++i) {
+            const int r = slot_row(i);
+            const int c = slot_col(i) ^ kswz<D>(r);
+            __builtin_amdgcn_global_load_lds(Kp + (int64_t)rows[i] * D + c * 8,
+                                             (lds_void *)(lds + stage * C::TILEB + (wave * C::INSTR + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+    auto issue_v = [&](int stage, const int (&rows)[C::INSTR]) {
+#pragma unroll
+        for (int i = 0; i < C::INSTR; ++i) {
+            const int r = slot_row(i);
+            const int c = slot_col(i) ^ vswz<D>(r);
+            __builtin_amdgcn_global_load_lds(Vp + (int64_t)rows[i] * D + c * 8,
+                                             (lds_void *)(lds + (2 + stage) * C::TILEB + (wave * C::INSTR + i) * 1024),
+                                             16, 0, 0);
+        }
+    };
+
+    // Q operand in registers (B operand of S^T = K Q^T)
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+        qf[s] = *reinterpret_cast<const bf16x8 *>(Qp + (int64_t)my_row * D + 16 * s + 8 * half);
+
+    constexpr int NACC = D / 32;
+    f32x16 acc[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const float c = a.scale_log2;
+
+    // per-lane LDS byte offsets of the operand reads
+    const int ka_off = li * C::ROWB, kb_off = (32 + li) * C::ROWB;
+    const int gi = lane >> 4, i16 = lane & 15;
+    const int v_h = gi >> 1, v_cg = gi & 1, v_e = i16 >> 2, v_rq = i16 & 3;
+
+    auto qk = [&](int stage, f32x16 &s0, f32x16 &s1, f32x16 &p0, f32x16 &p1, float m_new, bool exps) {
+        const unsigned char *Kt = lds + stage * C::TILEB;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
+        constexpr int STEPS = D / 16;
+        constexpr int EPS = 16 / STEPS;
+        bf16x8 ka[2], kb[2];
+        ka[0] = *reinterpret_cast<const bf16x8 *>(Kt + ka_off + ((half ^ kswz<D>(li)) << 4));
+        kb[0] = *reinterpret_cast<const bf16x8 *>(Kt + kb_off + ((half ^ kswz<D>(32 + li)) << 4));
+#pragma unroll
+        for (int st = 0; st < STEPS; ++st) {
+            if (st + 1 < STEPS) {
+                const int pc = 2 * (st + 1) + half;
+                ka[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kt + ka_off + ((pc ^ kswz<D>(li)) << 4));
+                kb[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kt + kb_off + ((pc ^ kswz<D>(32 + li)) << 4));
+            }
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1], qf[st], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[st & 1], qf[st], s1, 0, 0, 0);
+            if (exps) {
+#pragma unroll
+                for (int e = 0; e < EPS; ++e) {
+                    const int r = st * EPS + e;
+                    p0[r] = __builtin_amdgcn_exp2f(fmaf(p0[r], c, -m_new));
+                    p1[r] = __builtin_amdgcn_exp2f(fmaf(p1[r], c, -m_new));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // prologue: K_0, V_0, K_1 into their stages; S_0
+    fetch_rows(0, krows);
+    issue_k(0, krows);
+    issue_v(0, krows);
+    if (total > 1) {
+        fetch_rows(1, krows);
+        issue_k(1, krows);
+    }
+    if (total > 2) fetch_rows(2, krows);
+    if (total > 1) fetch_rows(1, vrows);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 s0, s1, dummy0, dummy1;
+    qk(0, s0, s1, dummy0, dummy1, 0.f, false);
+    __syncthreads();  // every wave has read K stage 0 before it is refilled
+
+    int executed2 = 0;
+    for (int k = 0; k < total; ++k) {
+        const int kst = k & 1;
+        if (k + 2 < total) issue_k(kst, krows);            // K_{k+2} -> stage of K_k
+        if (k + 1 < total) issue_v(kst ^ 1, vrows);        // V_{k+1} -> stage of V_{k-1}
+        if (k + 3 < total) fetch_rows(k + 3, krows);
+        if (k + 2 < total) fetch_rows(k + 2, vrows);
+
+        const bool is_p2 = S2O && k >= n1;
+        const int key0 = is_p2 ? 0 : base1 + k * BN;
+        if (!is_p2 && g.causal && key0 + BN - 1 > row0 + 32 * wave) mask_chunk(s0, s1, key0, my_row, half);
+        const float mx = pair_max(fmaxf(max16(s0), max16(s1))) * c;
+        const float m_new = mx > m + kMaxSlack ? mx : m;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+
+        // phase 1: S_{k+1} on the matrix cores with the exponentials of chunk k
+        // (stale stage when k+1 == total; the result is unused then)
+        f32x16 sn0, sn1;
+        qk(kst ^ 1, sn0, sn1, s0, s1, m_new, true);
+        rescale(acc, alpha);
+
+        // phase 2: O^T += V^T P^T for chunk k with the row sum
+        float sum = 0.f;
+        {
+            const unsigned char *Vt = lds + (2 + kst) * C::TILEB;
+            bf16x8 pb[4];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pb[0][e] = (__bf16)s0[e];
+                pb[1][e] = (__bf16)s0[8 + e];
+                pb[2][e] = (__bf16)s1[e];
+                pb[3][e] = (__bf16)s1[8 + e];
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int key1 = 16 * s + 4 * v_h + v_e;
+#pragma unroll
+                for (int cb = 0; cb < NACC; ++cb) {
+                    const int col = 32 * cb + 16 * v_cg + 4 * v_rq;
+                    const int within = (col & 7) * 2;
+                    const int a1 = key1 * C::ROWB + ((((col >> 3) ^ vswz<D>(key1))) << 4) + within;
+                    const int a2 = (key1 + 8) * C::ROWB + ((((col >> 3) ^ vswz<D>(key1 + 8))) << 4) + within;
+                    v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16 *)(Vt + a1));
+                    v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16 *)(Vt + a2));
+                    bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum += s0[4 * s + e] + s1[4 * s + e];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        const float delta = pair_sum(sum);
+        l = l * alpha + delta;
+        const bool wave_cont = is_p2 && __ballot(!(delta < a.tau * l)) != 0;
+
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's K_{k+2} / V_{k+1} pieces and indices landed
+        if (is_p2 && lane == 0) flags[kst][wave] = wave_cont ? 1 : 0;
+        __syncthreads();
+        if (is_p2) {
+            executed2 = k - n1 + 1;
+            int any = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) any |= flags[kst][w];
+            if (!any) break;
+        }
+        s0 = sn0;
+        s1 = sn1;
+    }
+
+    const float inv = 1.0f / l;
+    __bf16 *Op = reinterpret_cast<__bf16 *>(a.o) + ((int64_t)(b * g.Hq + h) * g.N + my_row) * D;
+#pragma unroll
+    for (int cb = 0; cb < NACC; ++cb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][4 * q + e] * inv));
+            *reinterpret_cast<u32x2 *>(Op + 32 * cb + 8 * q + 4 * half) = u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+        }
+    }
+    if (a.exec && tid == 0) a.exec[((int64_t)b * g.Hq + h) * g.T + t] = n1 + executed2;
+}
+
+template <int D, int NW, bool S2O>
+hipError_t launch_bf16(const AttnParams &p, hipStream_t stream) {
+    using C = BCfg<D, NW, S2O>;
     const Geometry &g = p.g;
     static bool attr_set = false;  // benign race: setting the same value twice is harmless
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel<T, D, NW, S2O>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel_bf16<D, NW, S2O>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     int64_t units = (int64_t)g.B * g.Hkv * g.T;
     int64_t blocks = ((units + 7) / 8) * 8 * g.G;
-    hipLaunchKernelGGL((attn_kernel<T, D, NW, S2O>), dim3((unsigned)blocks), dim3(C::NT),
+    hipLaunchKernelGGL((attn_kernel_bf16<D, NW, S2O>), dim3((unsigned)blocks), dim3(C::NT), C::LDS_BYTES,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int NW, bool S2O>
+hipError_t launch_one(const AttnParams &p, hipStream_t stream) {
+    using C = Cfg<T, D, NW, S2O>;
+    const Geometry &g = p.g;
+    static bool attr_set = false;  // benign race: setting the same value twice is harmless
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel_staged<T, D, NW, S2O>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    int64_t units = (int64_t)g.B * g.Hkv * g.T;
+    int64_t blocks = ((units + 7) / 8) * 8 * g.G;
+    hipLaunchKernelGGL((attn_kernel_staged<T, D, NW, S2O>), dim3((unsigned)blocks), dim3(C::NT),
                        C::LDS_BYTES, stream, p);
     return hipGetLastError();
 }
@@ -464,8 +835,13 @@ hipError_t launch_attention(const Geometry &g, const void *Q, const void *K, con
     p.g = g;
     p.scale_log2 = g.scale * 1.4426950408889634f;
     p.tau = tau;
-    if (g.dtype == 1)
-        return s2o ? launch_d<__bf16, true>(p, stream) : launch_d<__bf16, false>(p, stream);
+    if (g.dtype == 1) {
+        if (g.d == 128)
+            return g.BM == 128 ? (s2o ? launch_bf16<128, 4, true>(p, stream) : launch_bf16<128, 4, false>(p, stream))
+                               : (s2o ? launch_bf16<128, 2, true>(p, stream) : launch_bf16<128, 2, false>(p, stream));
+        return g.BM == 128 ? (s2o ? launch_bf16<64, 4, true>(p, stream) : launch_bf16<64, 4, false>(p, stream))
+                           : (s2o ? launch_bf16<64, 2, true>(p, stream) : launch_bf16<64, 2, false>(p, stream));
+    }
     return s2o ? launch_d<float, true>(p, stream) : launch_d<float, false>(p, stream);
 }
 

@@ -45,7 +45,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("N", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("seg_len", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("tile_n", ctypes.c_int32), ("scale", ctypes.c_double)]
+                ("tile_n", ctypes.c_int32), ("scale", ctypes.c_double),
+                ("per_segment", ctypes.c_int32)]
 
 
 _lib = None
@@ -66,6 +67,7 @@ def _load():
             "oracle_list_offset": (i64, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
             "oracle_list_entries": (i64, [P]),
             "oracle_pool": (None, [P, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
+            "oracle_rep_query": (None, [P, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
             "oracle_score_tile": (None, [P, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
             "oracle_order": (None, [vp, i64, vp]),
             "oracle_attn_tile": (i32, [P, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -86,15 +88,17 @@ def _load():
     return _lib
 
 
-def problem(B, Hq, Hkv, N, d, dtype, seg_len, tile_m, tile_n, scale) -> Problem:
-    """dtype: "f32" (float32 arrays) or "bf16" (uint16 bit-pattern arrays)."""
+def problem(B, Hq, Hkv, N, d, dtype, seg_len, tile_m, tile_n, scale, per_segment=False) -> Problem:
+    """dtype: "f32" (float32 arrays) or "bf16" (uint16 bit-pattern arrays).
+    per_segment: one list per segment (shared by its tiles) instead of per tile."""
     return Problem(B, Hq, Hkv, N, d, 0 if dtype == "f32" else 1, seg_len, tile_m, tile_n,
-                   float(scale))
+                   float(scale), 1 if per_segment else 0)
 
 
-def problem_from_workload(w, seg_len=None) -> Problem:
+def problem_from_workload(w, seg_len=None, per_segment=False) -> Problem:
     return problem(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype,
-                   w.seg_len if seg_len is None else seg_len, w.tile_m, w.tile_n, w.scale)
+                   w.seg_len if seg_len is None else seg_len, w.tile_m, w.tile_n, w.scale,
+                   per_segment)
 
 
 def _ptr(a):
@@ -135,6 +139,13 @@ def num_threads():
 def pool(p, Q, b, h, t):
     out = np.empty(p.d, dtype=np.float32)
     _load().oracle_pool(ctypes.byref(p), _ptr(_check(Q, p, "Q")), b, h, t, _ptr(out))
+    return out
+
+
+def rep_query(p, Q, b, h, t):
+    """The representative query of the list tile t uses (tile mean or segment mean)."""
+    out = np.empty(p.d, dtype=np.float32)
+    _load().oracle_rep_query(ctypes.byref(p), _ptr(_check(Q, p, "Q")), b, h, t, _ptr(out))
     return out
 
 

@@ -30,6 +30,12 @@
  *              order, part of the definition so that any faithful evaluation
  *              gives the same bits).  Only causal-prefix keys are scored
  *              ([GIST] KV_perm).
+ *   segment lists (optional granularity): one list per (b, h, segment), shared
+ *              by the segment's tiles, scored against the segment's
+ *              representative query ([GIST] KV_perm speaks of a
+ *              representative query of the segment): the mean of the
+ *              segment's tile queries, an fp32 sum over its tiles in
+ *              ascending order times fl(1/number of tiles).
  *   order      the list: history keys sorted by score descending, ties to the
  *              lower index ([GIST] KV_perm: indices form a global logical map).
  *   pass 1     for each row i, online softmax over keys [a_t, i] in BN-wide key
@@ -67,6 +73,7 @@ typedef struct {
     int32_t dtype; /* 0: fp32 values, 1: bf16 bit patterns (uint16) */
     int32_t seg_len, tile_m, tile_n;
     double scale;
+    int32_t per_segment; /* 0: one list per query tile; 1: one list per segment */
 } oracle_problem;
 
 /* ---- element access ------------------------------------------------------ */
@@ -103,21 +110,35 @@ int32_t oracle_pass1_tiles(const oracle_problem *p, int t) {
     return (int32_t)((end - a + p->tile_n - 1) / p->tile_n);
 }
 
-/* Offsets of the per-tile lists, ordered by (b, h, t).  Computed by walking
- * the tiles and adding their history lengths; lists of segment-0 tiles are
- * empty. */
+/* Offsets of the lists.  Per-tile lists are ordered by (b, h, t); per-segment
+ * lists by (b, h, segment) and tile t uses the list of its segment.  Computed
+ * by walking the lists and adding their history lengths; lists of segment 0
+ * are empty. */
+static int32_t num_segments(const oracle_problem *p) { return (p->N + p->seg_len - 1) / p->seg_len; }
+
+static int64_t per_head_entries(const oracle_problem *p) {
+    int64_t total = 0;
+    if (p->per_segment) {
+        for (int s = 0; s < num_segments(p); ++s) total += (int64_t)s * p->seg_len;
+    } else {
+        for (int u = 0; u < oracle_num_tiles(p); ++u) total += oracle_seg_start(p, u);
+    }
+    return total;
+}
+
 int64_t oracle_list_offset(const oracle_problem *p, int b, int h, int t) {
-    int32_t T = oracle_num_tiles(p);
-    int64_t per_head = 0;
-    for (int u = 0; u < T; ++u) per_head += oracle_seg_start(p, u);
-    int64_t off = ((int64_t)b * p->Hq + h) * per_head;
-    for (int u = 0; u < t; ++u) off += oracle_seg_start(p, u);
+    int64_t off = ((int64_t)b * p->Hq + h) * per_head_entries(p);
+    if (p->per_segment) {
+        int seg = (int)(oracle_seg_start(p, t) / p->seg_len);
+        for (int s = 0; s < seg; ++s) off += (int64_t)s * p->seg_len;
+    } else {
+        for (int u = 0; u < t; ++u) off += oracle_seg_start(p, u);
+    }
     return off;
 }
 
 int64_t oracle_list_entries(const oracle_problem *p) {
-    return oracle_list_offset(p, p->B - 1, p->Hq - 1, oracle_num_tiles(p) - 1) +
-           oracle_seg_start(p, oracle_num_tiles(p) - 1);
+    return (int64_t)p->B * p->Hq * per_head_entries(p);
 }
 
 /* ---- estimator: pool and score ------------------------------------------- */
@@ -135,13 +156,37 @@ void oracle_pool(const oracle_problem *p, const void *Q, int b, int h, int t, fl
     }
 }
 
-/* Scores of tile t's history keys: s[j] = fmaf chain over k = 0..d-1. */
+/* Representative query of the list tile t uses: the tile's mean, or (segment
+ * lists) the mean of the segment's tile means: fp32 sum over the segment's
+ * tiles in ascending order, then one multiplication by fl(1/number of tiles). */
+void oracle_rep_query(const oracle_problem *p, const void *Q, int b, int h, int t, float *qbar) {
+    if (!p->per_segment) {
+        oracle_pool(p, Q, b, h, t, qbar);
+        return;
+    }
+    int P = p->seg_len / p->tile_m;
+    int first = (int)(oracle_seg_start(p, t) / p->tile_m);
+    int last = first + P;
+    if (last > oracle_num_tiles(p)) last = oracle_num_tiles(p);
+    float *tq = (float *)malloc(sizeof(float) * p->d);
+    for (int k = 0; k < p->d; ++k) qbar[k] = 0.0f;
+    for (int u = first; u < last; ++u) {
+        oracle_pool(p, Q, b, h, u, tq);
+        for (int k = 0; k < p->d; ++k) qbar[k] = qbar[k] + tq[k];
+    }
+    float inv = 1.0f / (float)(last - first);
+    for (int k = 0; k < p->d; ++k) qbar[k] = qbar[k] * inv;
+    free(tq);
+}
+
+/* Scores of the history keys of the list tile t uses: s[j] = fmaf chain over
+ * k = 0..d-1. */
 void oracle_score_tile(const oracle_problem *p, const void *Q, const void *K, int b, int h,
                        int t, float *scores) {
     int g = h / (p->Hq / p->Hkv);
     int64_t a = oracle_seg_start(p, t);
     float *qbar = (float *)malloc(sizeof(float) * p->d);
-    oracle_pool(p, Q, b, h, t, qbar);
+    oracle_rep_query(p, Q, b, h, t, qbar);
     for (int64_t j = 0; j < a; ++j) {
         float acc = 0.0f;
         for (int k = 0; k < p->d; ++k) acc = fmaf(qbar[k], widen(K, p->dtype, kv_index(p, b, g, j, k)), acc);
@@ -314,25 +359,37 @@ int oracle_num_threads(void) {
 #endif
 }
 
-/* scores of every tile, in the (b, h, t) list layout */
+/* The tile that owns list number u of a head: the tile itself (tile lists) or
+ * the first tile of segment u (segment lists). */
+static int list_owner(const oracle_problem *p, int u) {
+    return p->per_segment ? u * (p->seg_len / p->tile_m) : u;
+}
+
+static int lists_per_head(const oracle_problem *p) {
+    return p->per_segment ? num_segments(p) : oracle_num_tiles(p);
+}
+
+/* scores of every list, in the list layout */
 void oracle_scores_all(const oracle_problem *p, const void *Q, const void *K, float *scores) {
-    int32_t T = oracle_num_tiles(p);
-    int64_t units = (int64_t)p->B * p->Hq * T;
+    int32_t U = lists_per_head(p);
+    int64_t units = (int64_t)p->B * p->Hq * U;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t u = 0; u < units; ++u) {
-        int b = (int)(u / ((int64_t)p->Hq * T)), h = (int)((u / T) % p->Hq), t = (int)(u % T);
+        int b = (int)(u / ((int64_t)p->Hq * U)), h = (int)((u / U) % p->Hq);
+        int t = list_owner(p, (int)(u % U));
         if (oracle_seg_start(p, t) > 0)
             oracle_score_tile(p, Q, K, b, h, t, scores + oracle_list_offset(p, b, h, t));
     }
 }
 
-/* lists of every tile from the scores */
+/* every list from the scores */
 void oracle_lists_all(const oracle_problem *p, const float *scores, int32_t *lists) {
-    int32_t T = oracle_num_tiles(p);
-    int64_t units = (int64_t)p->B * p->Hq * T;
+    int32_t U = lists_per_head(p);
+    int64_t units = (int64_t)p->B * p->Hq * U;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t u = 0; u < units; ++u) {
-        int b = (int)(u / ((int64_t)p->Hq * T)), h = (int)((u / T) % p->Hq), t = (int)(u % T);
+        int b = (int)(u / ((int64_t)p->Hq * U)), h = (int)((u / U) % p->Hq);
+        int t = list_owner(p, (int)(u % U));
         int64_t off = oracle_list_offset(p, b, h, t);
         oracle_order(scores + off, oracle_seg_start(p, t), lists + off);
     }

@@ -45,6 +45,8 @@ MUTANTS = {
         "dot += (double)widen(Q, p->dtype, q_index(p, b, h, j, k)) *\n"
         "               (double)widen(K, p->dtype, kv_index(p, b, g, i, k));"),
     "pass 2 skips its first chunk": ("for (int32_t c = 0; c < limit; ++c) {", "for (int32_t c = 1; c < limit; ++c) {"),
+    "segment mean drops its last tile": ("for (int u = first; u < last; ++u) {", "for (int u = first; u < last - 1; ++u) {"),
+    "segment lists keyed by tile": ("int seg = (int)(oracle_seg_start(p, t) / p->seg_len);", "int seg = t % num_segments(p);"),
 }
 
 

@@ -446,3 +446,75 @@ def test_force_n_runs_the_requested_chunk_count():
             x = p.scale * (Kd[0, 0, ks] @ Qd[0, 0, i])
             w = np.exp(x - x.max())
             np.testing.assert_allclose(out[r_], (w / w.sum()) @ Vd[0, 0, ks], atol=1e-12)
+
+
+# ------------------------------------------------------------ segment lists ---
+# One list per (b, h, segment), shared by the segment's tiles and scored against
+# the segment's representative query (gist.science summary, "Classement par
+# Segment": history keys are scored against a representative query of the
+# segment).
+
+@pytest.mark.parametrize("geom", GEOMS)
+def test_segment_lists_tau_zero_equals_dense_attention(geom):
+    B, Hq, Hkv, N, d, S, BM, BN, dt = geom
+    Q, K, V = random_inputs(B, Hq, Hkv, N, d, seed=121 + N, dtype=dt)
+    p = oracle.problem(B, Hq, Hkv, N, d, dt, S, BM, BN, 1 / np.sqrt(d), per_segment=True)
+    out, _, chunks, _ = run_all(p, Q, K, V, 0.0)
+    np.testing.assert_allclose(out, sdpa_fp64(p, Q, K, V), rtol=0, atol=1e-12)
+
+
+def test_segment_list_layout_and_sharing():
+    """Offsets walk (b, h, segment); every tile of a segment uses the same list, equal to
+    the order of the segment representative's scores."""
+    Q, K, V = random_inputs(2, 4, 2, 200, 16, seed=13)
+    S, BM = 48, 8
+    p = oracle.problem(2, 4, 2, 200, 16, "f32", S, BM, 8, 0.25, per_segment=True)
+    nseg = (200 + S - 1) // S
+    L = sum(s * S for s in range(nseg))
+    assert oracle.list_entries(p) == 2 * 4 * L
+    scores = oracle.scores_all(p, Q, K)
+    lists = oracle.lists_all(p, scores)
+    T = 200 // BM
+    for b in (0, 1):
+        for h in (0, 3):
+            for t in range(T):
+                s = t * BM // S
+                off = oracle.list_offset(p, b, h, t)
+                assert off == (b * 4 + h) * L + S * s * (s - 1) // 2
+                a = oracle.seg_start(p, t)
+                sc = oracle.score_tile(p, Q, K, b, h, t)
+                assert np.array_equal(scores[off:off + a], sc)
+                assert np.array_equal(lists[off:off + a], oracle.order(sc))
+
+
+def test_segment_representative_is_the_mean_of_its_rows():
+    """fp64 mean of the segment's rows, within the two-level fp32 summation bound; the
+    last (partial) segment averages only its own tiles."""
+    Q, _, _ = random_inputs(1, 2, 1, 200, 16, seed=17, dtype="bf16")
+    S, BM = 48, 8
+    p = oracle.problem(1, 2, 1, 200, 16, "bf16", S, BM, 8, 0.25, per_segment=True)
+    Qd = widen(Q, p)
+    u = 2.0 ** -24
+    for h in range(2):
+        for t in (6, 7, 12, 24):
+            s0 = t * BM // S * S
+            s1 = min(s0 + S, 200)
+            rows = Qd[0, h, s0:s1]
+            got = oracle.rep_query(p, Q, 0, h, t).astype(np.float64)
+            bound = 4 * (BM + (s1 - s0) // BM) * u * np.abs(rows).mean(axis=0) + 1e-30
+            assert np.all(np.abs(got - rows.mean(axis=0)) <= bound)
+
+
+def test_segment_representative_exact_on_dyadic_inputs():
+    """Constant integer rows per tile and a power-of-two tile count: every fp32 operation
+    is exact, so the representative equals the exact mean of the tile values."""
+    N, d, BM, S = 128, 4, 8, 32
+    rng = np.random.default_rng(2)
+    vals = rng.integers(-6, 7, size=(N // BM, d)).astype(np.float32)
+    Q = np.repeat(vals, BM, axis=0).reshape(1, 1, N, d).astype(np.float32)
+    p = oracle.problem(1, 1, 1, N, d, "f32", S, BM, 8, 1.0, per_segment=True)
+    for t in range(N // BM):
+        first = t * BM // S * (S // BM)
+        want = [Fraction(int(x)) for x in vals[first:first + S // BM].astype(np.int64).sum(axis=0)]
+        want = [w / (S // BM) for w in want]
+        assert [Fraction(float(x)) for x in oracle.rep_query(p, Q, 0, 0, t)] == want

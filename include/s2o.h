@@ -34,10 +34,12 @@
  *   segment starts at a_t = floor(t*BM / S) * S; its history is keys [0, a_t).
  *
  * List layout (scores and idx)
- *   One list per (b, h, t), concatenated in (b, h, t) row-major order; tile t's
- *   list has a_t entries (segment-0 lists are empty).  With P = S / BM,
- *   s = floor(t / P) and L = one head's total,
+ *   Per-tile lists: one per (b, h, t), concatenated in (b, h, t) row-major
+ *   order; tile t's list has a_t entries (segment-0 lists are empty).  With
+ *   P = S / BM, s = floor(t / P) and L = one head's total,
  *     off(b, h, t) = (b*Hq + h)*L + S*(P*s*(s-1)/2 + (t - s*P)*s).
+ *   Per-segment lists: one per (b, h, s), list s has s*S entries,
+ *     off(b, h, s) = (b*Hq + h)*L + S*s*(s-1)/2, and tile t uses list floor(t/P).
  *   Entries are int64-addressed; idx values are key positions in [0, a_t).
  */
 #ifndef S2O_H
@@ -73,31 +75,42 @@ typedef struct {
     int32_t tile_m;   /* BM: 64 or 128 */
     int32_t tile_n;   /* BN: 64 */
     float scale;      /* softmax scale (1/sqrt(d) for standard attention), finite */
+    int32_t list_granularity; /* S2O_LISTS_PER_TILE (0) or S2O_LISTS_PER_SEGMENT (1) */
 } s2o_problem;
+
+/* Which query a list is ranked against ([GIST] KV_perm):
+ *   S2O_LISTS_PER_TILE: one list per (b, h, query tile), ranked against the
+ *     tile's mean query;
+ *   S2O_LISTS_PER_SEGMENT: one list per (b, h, segment), shared by the
+ *     segment's tiles and ranked against the segment's representative query =
+ *     fp32 sum of its tile means in ascending tile order times fl(1/tiles). */
+enum { S2O_LISTS_PER_TILE = 0, S2O_LISTS_PER_SEGMENT = 1 };
 
 /* Validates a problem (sizes, divisibility, supported tiles).  Returns S2O_OK,
  * S2O_ERR_INVALID_ARG or S2O_ERR_UNSUPPORTED.  Pure host function. */
 s2o_status s2o_check_problem(const s2o_problem *p);
 
-/* Total list entries over all (b, h, t): B*Hq*sum_t a_t.  -1 if the problem is
- * invalid.  Pure host function. */
+/* Total list entries over all lists (per tile: B*Hq*sum_t a_t; per segment:
+ * B*Hq*sum_s s*S).  -1 if the problem is invalid.  Pure host function. */
 int64_t s2o_list_entries(const s2o_problem *p);
 
-/* Offset of the list of (b, h, t) in the layout above; -1 if out of range or
- * the problem is invalid.  Pure host function. */
+/* Offset of the list tile t of (b, h) uses, in the layout above; -1 if out of
+ * range or the problem is invalid.  Pure host function. */
 int64_t s2o_list_offset(const s2o_problem *p, int32_t b, int32_t h, int32_t t);
 
-/* Bytes of device workspace s2o_score needs (the pooled query of every tile,
- * fp32).  0 if the problem is invalid. */
+/* Bytes of device workspace s2o_score needs (the pooled query of every tile
+ * and, for per-segment lists, of every segment, fp32).  0 if the problem is
+ * invalid. */
 size_t s2o_score_workspace_bytes(const s2o_problem *p);
 
 /* Importance estimator ([GIST] KV_perm: history keys are scored against a
- * representative query; only causal-prefix keys count).  For every tile with
- * history, qbar = mean of the tile's BM query rows (fp32 sum over rows in
- * ascending order, then an exact scaling by 1/BM) and
- *   scores[off(b,h,t) + j] = fp32 fma chain over k = 0..d-1 of qbar[k] * K[b, h/G, j, k],
- * accumulated from 0 in ascending k, for j in [0, a_t).  This order is part of
- * the definition, so results are bit-reproducible.
+ * representative query; only causal-prefix keys count).  For every list with
+ * history: qbar = the tile's mean query (fp32 sum over its BM rows in ascending
+ * order, then an exact scaling by 1/BM) or, for per-segment lists, the
+ * segment's representative described above; then
+ *   scores[off + j] = fp32 fma chain over k = 0..d-1 of qbar[k] * K[b, h/G, j, k],
+ * accumulated from 0 in ascending k, for j in [0, history length).  This order
+ * is part of the definition, so results are bit-reproducible.
  *   Q, K: device, problem dtype.  scores: device fp32 [s2o_list_entries].
  *   workspace: device, >= s2o_score_workspace_bytes, 256-byte aligned.
  * Errors: INVALID_ARG, UNSUPPORTED (causal = 0), WORKSPACE, HIP. */
@@ -108,9 +121,10 @@ s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *
 size_t s2o_build_index_workspace_bytes(const s2o_problem *p);
 
 /* Index build ([GIST] KV_perm: the resulting indices form a global logical map
- * that puts likely vertical and slash stripes first).  For every tile, idx
- * receives the positions [0, a_t) sorted by score descending, ties broken by
- * the lower position; -0.0 and +0.0 tie.  A segmented stable radix sort.
+ * that puts likely vertical and slash stripes first).  For every list, idx
+ * receives the positions [0, history length) sorted by score descending, ties
+ * broken by the lower position; -0.0 and +0.0 tie.  A segmented stable radix
+ * sort.
  *   scores: device fp32 [s2o_list_entries] (from s2o_score).
  *   idx: device int32 [s2o_list_entries].
  *   workspace: device, >= s2o_build_index_workspace_bytes, 256-byte aligned.
@@ -122,8 +136,8 @@ s2o_status s2o_build_index(const s2o_problem *p, const float *scores, int32_t *i
  * [GIST] 2. Règle d'Arrêt Anticipé; [ABS]).  Per tile t and row i:
  *   pass 1: online softmax over keys [a_t, i] (dense causal window inside the
  *           segment), initialising (m, l, acc);
- *   pass 2: for chunks c = 0, 1, ... of BN consecutive entries of the tile's
- *           list, gather those K/V rows, update (m, l, acc), and take the chunk
+ *   pass 2: for chunks c = 0, 1, ... of BN consecutive entries of the list the
+ *           tile uses, gather those K/V rows, update (m, l, acc), and take the chunk
  *           mass delta_i = sum exp(x_ij - m_i) against the updated max; stop
  *           after chunk c when delta_i < tau * l_i (l after the chunk) for every
  *           row of the tile.  The stopping chunk is kept; tau = 0 never stops.

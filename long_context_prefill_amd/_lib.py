@@ -40,7 +40,7 @@ class Problem(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("seg_len", ctypes.c_int32),
                 ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("list_granularity", ctypes.c_int32)]
 
     def astuple(self):
         return tuple(getattr(self, f) for f, _ in self._fields_)
@@ -84,21 +84,27 @@ def _raise(fn: str, st: int):
         raise S2OError(fn, st, lib().s2o_status_string(st).decode())
 
 
+LISTS_PER_TILE, LISTS_PER_SEGMENT = 0, 1
+
+
 def problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, seg_len, tile_m=128,
-            tile_n=64, scale=None, causal=True) -> Problem:
-    """dtype: torch.float32 / torch.bfloat16 (or 0 / 1)."""
+            tile_n=64, scale=None, causal=True, lists="tile") -> Problem:
+    """dtype: torch.float32 / torch.bfloat16 (or 0 / 1).
+    lists: "tile" (one list per query tile) or "segment" (one list per segment)."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
+    gran = {"tile": LISTS_PER_TILE, "segment": LISTS_PER_SEGMENT}[lists]
     return Problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, 1 if causal else 0,
-                   seg_len, tile_m, tile_n, float(scale))
+                   seg_len, tile_m, tile_n, float(scale), gran)
 
 
 def problem_for(q: torch.Tensor, k: torch.Tensor, seg_len: int, tile=(128, 64), scale=None,
-                causal=True) -> Problem:
+                causal=True, lists="tile") -> Problem:
     B, Hq, N, d = q.shape
-    return problem(B, Hq, k.shape[1], N, d, q.dtype, seg_len, tile[0], tile[1], scale, causal)
+    return problem(B, Hq, k.shape[1], N, d, q.dtype, seg_len, tile[0], tile[1], scale, causal,
+                   lists)
 
 
 def _stream() -> ctypes.c_void_p:
@@ -208,9 +214,9 @@ def dense_attn_fwd(p: Problem, q, k, v, out=None) -> torch.Tensor:
     return out
 
 
-def s2o_attention(q, k, v, tau: float, seg_len: int, tile=(128, 64), scale=None):
+def s2o_attention(q, k, v, tau: float, seg_len: int, tile=(128, 64), scale=None, lists="tile"):
     """Whole path: score -> build_index -> attention.  Returns (O, exec_tiles)."""
-    p = problem_for(q, k, seg_len, tile, scale)
+    p = problem_for(q, k, seg_len, tile, scale, lists=lists)
     scores = s2o_score(p, q, k)
     idx = s2o_build_index(p, scores)
     return s2o_attn_fwd(p, q, k, v, idx, tau)

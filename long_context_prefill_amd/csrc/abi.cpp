@@ -30,6 +30,8 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     if (p->head_dim != 64 && p->head_dim != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_m != 64 && p->tile_m != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_n != s2o::kTileN) return S2O_ERR_UNSUPPORTED;
+    if (p->list_granularity != S2O_LISTS_PER_TILE && p->list_granularity != S2O_LISTS_PER_SEGMENT)
+        return S2O_ERR_INVALID_ARG;
 
     g.B = p->batch;
     g.Hq = p->heads_q;
@@ -45,13 +47,17 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     g.causal = p->causal;
     g.dtype = p->dtype;
     g.scale = p->scale;
-    // L = sum_t a_t: walk the segments
+    g.per_seg = p->list_granularity == S2O_LISTS_PER_SEGMENT;
+    g.nseg = (g.N + g.S - 1) / g.S;
+    g.inv_P = 1.0f / (float)g.P;
+    g.inv_P_last = 1.0f / (float)(g.T - (g.nseg - 1) * g.P);
+    // L: history entries of one head's lists, walking the segments
     int64_t L = 0;
-    for (int64_t s = 0; s * g.S < g.N; ++s) {
+    for (int64_t s = 0; s < g.nseg; ++s) {
         int64_t tiles = (int64_t)g.P;
         int64_t first = s * g.P;
         if (first + tiles > g.T) tiles = g.T - first;
-        L += tiles * s * g.S;
+        L += (g.per_seg ? 1 : tiles) * s * g.S;
     }
     g.list_per_head = L;
     g.list_entries = L * g.B * g.Hq;
@@ -97,10 +103,15 @@ int64_t s2o_list_offset(const s2o_problem *p, int32_t b, int32_t h, int32_t t) {
     return s2o::list_offset(g, b, h, t);
 }
 
+namespace {
+size_t tile_query_bytes(const Geometry &g) { return ((size_t)g.B * g.Hq * g.T * g.d * sizeof(float) + 255) & ~(size_t)255; }
+}
+
 size_t s2o_score_workspace_bytes(const s2o_problem *p) {
     Geometry g;
     if (make_geometry(p, g) != S2O_OK) return 0;
-    return (size_t)g.B * g.Hq * g.T * g.d * sizeof(float);
+    size_t seg = g.per_seg ? (size_t)g.B * g.Hq * g.nseg * g.d * sizeof(float) : 0;
+    return tile_query_bytes(g) + seg;
 }
 
 s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *scores,
@@ -115,9 +126,11 @@ s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *
     if (g.list_entries == 0) return S2O_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float *qbar = reinterpret_cast<float *>(workspace);
-    hipError_t e = s2o::launch_pool(g, Q, qbar, s);
+    float *qseg = g.per_seg ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + tile_query_bytes(g))
+                            : nullptr;
+    hipError_t e = s2o::launch_pool(g, Q, qbar, qseg, s);
     if (e != hipSuccess) return S2O_ERR_HIP;
-    return launch_status(s2o::launch_score(g, qbar, K, scores, s));
+    return launch_status(s2o::launch_score(g, g.per_seg ? qseg : qbar, K, scores, s));
 }
 
 size_t s2o_build_index_workspace_bytes(const s2o_problem *p) {
@@ -156,7 +169,10 @@ s2o_status dense_attn_fwd(const s2o_problem *p, const void *Q, const void *K, co
                           void *O, void *stream) {
     Geometry g;
     s2o_problem q = p ? *p : s2o_problem{};
-    if (p) q.seg_len = p->seq_len;  // one segment: the dense schedule has no lists
+    if (p) {
+        q.seg_len = p->seq_len;  // one segment: the dense schedule has no lists
+        q.list_granularity = S2O_LISTS_PER_TILE;
+    }
     s2o_status st = make_geometry(p ? &q : nullptr, g);
     if (st != S2O_OK) return st;
     if (!Q || !K || !V || !O || !aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))

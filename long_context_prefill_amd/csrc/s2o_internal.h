@@ -16,17 +16,27 @@ struct Geometry {
     int32_t B, Hq, Hkv, G, N, d, S, BM, BN, T, P;  // P = S / BM tiles per segment
     int32_t causal;
     int32_t dtype;           // 0 fp32, 1 bf16
+    int32_t per_seg;         // lists per segment (1) or per query tile (0)
+    int32_t nseg;            // segments, the last one possibly partial
+    float inv_P, inv_P_last; // fl(1/tiles) of a full and of the last segment
     int64_t list_per_head;   // L: list entries of one (b, h)
     int64_t list_entries;    // B * Hq * L
     float scale;
 };
 
-// off(b,h,t) = (b*Hq+h)*L + S*(P*s*(s-1)/2 + (t - s*P)*s), s = t / P
+// Offset of the list tile t of (b, h) uses:
+//   per tile:    (b*Hq+h)*L + S*(P*s*(s-1)/2 + (t - s*P)*s), s = t / P
+//   per segment: (b*Hq+h)*L + S*s*(s-1)/2
 __host__ __device__ inline int64_t list_offset(const Geometry &g, int b, int h, int t) {
     int64_t s = t / g.P;
-    return ((int64_t)b * g.Hq + h) * g.list_per_head +
-           (int64_t)g.S * (g.P * s * (s - 1) / 2 + (t - s * g.P) * s);
+    int64_t within = g.per_seg ? (int64_t)g.S * (s * (s - 1) / 2)
+                               : (int64_t)g.S * (g.P * s * (s - 1) / 2 + (t - s * g.P) * s);
+    return ((int64_t)b * g.Hq + h) * g.list_per_head + within;
 }
+
+// Lists of one (b, h) and the tile owning list u (its first user).
+__host__ __device__ inline int lists_per_head(const Geometry &g) { return g.per_seg ? g.nseg : g.T; }
+__host__ __device__ inline int list_owner(const Geometry &g, int u) { return g.per_seg ? u * g.P : u; }
 
 __host__ __device__ inline int64_t seg_start(const Geometry &g, int t) {
     return ((int64_t)t * g.BM / g.S) * g.S;
@@ -37,8 +47,8 @@ hipError_t launch_attention(const Geometry &g, const void *Q, const void *K, con
                             const int32_t *idx, float tau, void *O, int32_t *exec_tiles,
                             bool s2o, hipStream_t stream);
 
-hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, hipStream_t stream);
-hipError_t launch_score(const Geometry &g, const float *qbar, const void *K, float *scores,
+hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, float *qseg, hipStream_t stream);
+hipError_t launch_score(const Geometry &g, const float *qrep, const void *K, float *scores,
                         hipStream_t stream);
 
 size_t sort_workspace_bytes(const Geometry &g);

@@ -6,8 +6,9 @@
 // prefix keys.  The representative is the mean of the tile's query rows.
 //
 // Scores are defined bit-exactly: qbar[k] = (fp32 sum of the BM rows in
-// ascending order) * (1/BM), then s[j] = fma chain over k = 0..d-1 starting
-// from 0.  The work is plain fp32 ALU (2*d flops per (tile, key) pair); the
+// ascending order) * (1/BM) (per-segment lists: fp32 sum of the segment's tile
+// means in ascending order times fl(1/tiles)), then s[j] = fma chain over
+// k = 0..d-1 starting from 0.  The work is plain fp32 ALU (2*d flops per (tile, key) pair); the
 // fixed accumulation order rules out matrix cores.
 //
 // Layout of the score kernel: one workgroup per (b, KV head, segment s >= 1,
@@ -46,6 +47,24 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, floa
     qbar[gid] = sum * (1.0f / (float)g.BM);  // exact: BM is a power of two
 }
 
+// Segment representatives (per-segment lists): mean of the segment's tile
+// means, an fp32 sum over its tiles in ascending order times fl(1/tiles).
+__global__ __launch_bounds__(256) void segpool_kernel(const float *__restrict__ qbar,
+                                                      float *__restrict__ qseg, Geometry g,
+                                                      int64_t total) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int k = (int)(gid % g.d);
+    const int64_t unit = gid / g.d;  // (b*Hq + h)*nseg + s
+    const int s = (int)(unit % g.nseg);
+    const int64_t bh = unit / g.nseg;
+    const int first = s * g.P;
+    const int last = min(g.T, first + g.P);
+    float sum = 0.0f;
+    for (int t = first; t < last; ++t) sum = sum + qbar[(bh * g.T + t) * g.d + k];
+    qseg[gid] = sum * (s == g.nseg - 1 ? g.inv_P_last : g.inv_P);
+}
+
 constexpr int SCORE_KEYS = 256;   // keys per workgroup (one per thread)
 constexpr int SCORE_ILP = 2;      // pairs evaluated together (independent fma chains)
 
@@ -61,7 +80,9 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
     if (s == 0 || j0 >= hist) return;
     const int b = bg / g.Hkv, kvh = bg % g.Hkv;
     const int t_first = s * g.P;
-    const int ntiles = min(g.T, (s + 1) * g.P) - t_first;
+    // per-tile lists: one pair per (query head, tile of the segment); per-segment
+    // lists: one pair per query head, ranked against the segment representative
+    const int ntiles = g.per_seg ? 1 : min(g.T, (s + 1) * g.P) - t_first;
     const int npairs = ntiles * g.G;             // pair p -> (query head kvh*G + p / ntiles, tile)
     const int j = j0 + (int)threadIdx.x;
     const bool live = j < hist;
@@ -102,7 +123,8 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
             const int pp = min(p0 + i, npairs - 1);
             const int hq = pp / ntiles;
             const int t = t_first + pp - hq * ntiles;
-            qp[i] = qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.T + t) * D;
+            qp[i] = g.per_seg ? qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.nseg + s) * D
+                              : qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.T + t) * D;
         }
         float acc[SCORE_ILP];
 #pragma unroll
@@ -126,7 +148,7 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
 
 }  // namespace
 
-hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, hipStream_t stream) {
+hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, float *qseg, hipStream_t stream) {
     int64_t total = (int64_t)g.B * g.Hq * g.T * g.d;
     unsigned blocks = (unsigned)((total + 255) / 256);
     if (g.dtype == 1)
@@ -135,6 +157,11 @@ hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, hipStream_
     else
         hipLaunchKernelGGL(pool_kernel<float>, dim3(blocks), dim3(256), 0, stream,
                            reinterpret_cast<const float *>(Q), qbar, g, total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !g.per_seg) return e;
+    int64_t stotal = (int64_t)g.B * g.Hq * g.nseg * g.d;
+    hipLaunchKernelGGL(segpool_kernel, dim3((unsigned)((stotal + 255) / 256)), dim3(256), 0, stream,
+                       qbar, qseg, g, stotal);
     return hipGetLastError();
 }
 

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(SORT_THREADS) void hist_kernel(const void *__restri
         hist[(int64_t)blockIdx.x * RADIX + v] = cnt[0][v] + cnt[1][v] + cnt[2][v] + cnt[3][v];
 }
 
-// One workgroup per list (b, h, t).  Turns the block histograms of the list
+// One workgroup per list.  Turns the block histograms of the list
 // into the start of each block's digit run, relative to the block's first
 // element: hist[bb][v] = (list_off + sum_{v'<v} total[v'] + sum_{bb'<bb} hist[bb'][v]) - bb*E.
 // The first pass also records each block's offset inside its list.
@@ -91,8 +91,9 @@ __global__ __launch_bounds__(RADIX) void scan_kernel(int32_t *__restrict__ hist,
                                                      int32_t *__restrict__ blk_pos, Geometry g,
                                                      int E, int first) {
     __shared__ int tot[RADIX];
-    const int t = blockIdx.x % g.T;
-    const int64_t bh = blockIdx.x / g.T;
+    const int U = lists_per_head(g);
+    const int t = list_owner(g, blockIdx.x % U);
+    const int64_t bh = blockIdx.x / U;
     const int64_t len = seg_start(g, t);
     if (len == 0) return;
     const int b = (int)(bh / g.Hq), h = (int)(bh % g.Hq);
@@ -245,7 +246,7 @@ template <int E>
 hipError_t run_sort(const Geometry &g, const float *scores, int32_t *idx, const SortWs &w,
                     hipStream_t stream) {
     const int64_t nblocks = g.list_entries / E;
-    const unsigned lists = (unsigned)((int64_t)g.B * g.Hq * g.T);
+    const unsigned lists = (unsigned)((int64_t)g.B * g.Hq * lists_per_head(g));
     // pass p: input keys/vals -> output keys/vals
     //   0: scores           -> keys_a, vals_a
     //   1: keys_a, vals_a   -> keys_b, idx      (idx doubles as scratch)

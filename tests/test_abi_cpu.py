@@ -61,6 +61,21 @@ def test_list_layout_matches_oracle_walk(N, S, BM, B, Hq):
     assert s2o.list_offset(p, 0, 0, T) == -1
 
 
+@pytest.mark.parametrize("N,S,BM,B,Hq", [(1024, 256, 128, 1, 4), (2048, 512, 64, 2, 3),
+                                         (64 * 63, 384, 64, 1, 2), (131072, 8192, 128, 1, 32)])
+def test_segment_list_layout_matches_oracle_walk(N, S, BM, B, Hq):
+    p = base_problem(batch=B, heads_q=Hq, heads_kv=1, seq_len=N, seg_len=S, tile_m=BM,
+                     lists="segment")
+    assert s2o.check_problem(p) == 0
+    po = oracle.problem(B, Hq, 1, N, 128, "bf16", S, BM, 64, 1.0, per_segment=True)
+    assert s2o.list_entries(p) == oracle.list_entries(po)
+    T = N // BM
+    for b in range(B):
+        for h in {0, Hq - 1}:
+            for t in sorted({0, T // 3, T // 2, T - 1}):
+                assert s2o.list_offset(p, b, h, t) == oracle.list_offset(po, b, h, t)
+
+
 def test_workspace_sizes():
     p = base_problem()
     assert s2o.score_workspace_bytes(p) == 1 * 4 * (1024 // 128) * 128 * 4
@@ -72,7 +87,7 @@ def test_workspace_sizes():
     ("batch", 0, INVALID), ("heads_q", 3, INVALID), ("seq_len", 1000, INVALID),
     ("seg_len", 200, INVALID), ("head_dim", 96, UNSUPPORTED), ("tile_m", 256, UNSUPPORTED),
     ("tile_n", 32, UNSUPPORTED), ("dtype", 7, INVALID), ("causal", 2, INVALID),
-    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID)])
+    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 2, INVALID)])
 def test_problem_validation(field, value, code):
     p = base_problem()
     setattr(p, field, value)

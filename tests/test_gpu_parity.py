@@ -273,3 +273,58 @@ def test_errors_raise_on_gpu():
         s2o.s2o_attn_fwd(p, q, q, q, idx, -1.0)
     with pytest.raises(ValueError):
         s2o.s2o_attn_fwd(p, q.float(), q, q, idx, 0.0)
+
+
+# ------------------------------------------------------------- segment lists --
+# One list per (b, h, segment), shared by the segment's tiles, ranked against
+# the segment's representative query.
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_bf16_segment_lists_every_tile(case):
+    name, B, Hq, Hkv, N, d, BM, S, structure = case
+    w = synth.custom_workload(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", tile_m=BM, tile_n=64,
+                              seg_len=S, structure=structure, n_stripes=max(N // 100, 4),
+                              seed=700 + N + d, name=name)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="segment")
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    for tau in (0.0, 1e-3, 3e-2):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, all_tiles(w), tau, o, ex, check_lists=False), "bf16")
+
+
+def test_tiny_f32_segment_lists():
+    w = synth.WORKLOADS["tiny_f32_n2048_s512"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="segment")
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    o, ex = run.attn(1e-3)
+    assert_report(compare(run, all_tiles(w), 1e-3, o, ex), "f32")
+
+
+def test_llama8b_16k_segment_lists():
+    w = synth.WORKLOADS["llama8b_n16k"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="segment")
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    tiles = sample_tiles(w, heads=(0, 9, 18, 27), n_random=16, seed=5)
+    for tau in (1e-2, 1e-3):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex, check_lists=False), "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_128k_segment_lists_sampled():
+    w = synth.WORKLOADS["llama8b_n128k"]
+    say("generating llama8b_n128k inputs")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="segment")
+    tiles = sample_tiles(w, heads=(3, 30), n_random=8, seed=6)
+    o, ex = run.attn(1e-3)
+    assert_report(compare(run, tiles, 1e-3, o, ex, check_lists=True), "bf16")

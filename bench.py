@@ -9,6 +9,10 @@ Before timing, tau is chosen as the largest value of a fixed sweep whose
 output stays within a dense-relative MSE of 1e-5 (MSE against this library's
 dense_attn_fwd over all B*Hq*N*d elements, fp32), unless --tau is given.
 
+The headline uses one index list per query tile.  The same measurement with
+one list per segment (shared by the segment's tiles) is reported under
+"segment_lists".
+
 Prints one JSON line (rank 0, one GPU).  Extra fields: per-phase times, the
 dense kernel's time, compute density, MSE, the MFMA roofline of the attention
 kernel (algorithmic flops of executed tiles / its average duration) and the
@@ -49,8 +53,10 @@ def parse():
     ap.add_argument("--workload", default="llama8b_n128k")
     ap.add_argument("--tau", type=float, default=None, help="skip the sweep and use this tau")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tiles", type=int, default=0, help="oracle sample size (0: 2 x threads)")
+    ap.add_argument("--cpu-tiles", type=int, default=0, help="oracle sample size (0: 8 x threads)")
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--tile-lists-only", action="store_true",
+                    help="skip the per-segment-list measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for profiles)")
     return ap.parse_args()
@@ -115,55 +121,86 @@ def main():
     dev = (lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)) \
         if w.dtype == "bf16" else (lambda a: torch.from_numpy(a).cuda())
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
-    p = s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0, w.seg_len,
-                    w.tile_m, w.tile_n, w.scale)
-    n_list = s2o.list_entries(p)
-    scores = torch.empty(n_list, dtype=torch.float32, device="cuda")
-    idx = torch.empty(n_list, dtype=torch.int32, device="cuda")
-    ws_score = torch.empty(max(s2o.score_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
-    ws_sort = torch.empty(max(s2o.build_index_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
-    out = torch.empty_like(q)
-    out_dense = torch.empty_like(q)
     T = w.N // w.tile_m
-    exec_tiles = torch.empty((w.B, w.Hq, T), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    dense_tiles = sum(((t + 1) * w.tile_m) // w.tile_n for t in range(T)) * w.B * w.Hq
+    flop_per_tile = 4.0 * w.tile_m * w.tile_n * w.d
 
-    def step(tau):
-        s2o.s2o_score(p, q, k, scores, ws_score)
-        s2o.s2o_build_index(p, scores, idx, ws_sort)
-        s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
-
-    # dense reference output and time
-    s2o.dense_attn_fwd(p, q, k, v, out_dense)
+    # dense reference output and time (the FlashAttention baseline)
+    p_dense = s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0, w.seg_len,
+                          w.tile_m, w.tile_n, w.scale)
+    out_dense = torch.empty_like(q)
+    s2o.dense_attn_fwd(p_dense, q, k, v, out_dense)
     torch.cuda.synchronize()
     dense_ms = []
     for _ in range(args.dense_reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        s2o.dense_attn_fwd(p, q, k, v, out_dense)
+        s2o.dense_attn_fwd(p_dense, q, k, v, out_dense)
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms.append(e0.elapsed_time(e1))
     dense_ms = float(np.median(dense_ms))
-    dense_tiles = sum(((t + 1) * w.tile_m) // w.tile_n for t in range(T)) * w.B * w.Hq
-    flop_per_tile = 4.0 * w.tile_m * w.tile_n * w.d
     log(f"dense_attn_fwd {dense_ms:.2f} ms ({dense_tiles * flop_per_tile / dense_ms / 1e9:.0f} TFLOP/s)")
-
-    # tau sweep (untimed)
-    s2o.s2o_score(p, q, k, scores, ws_score)
-    s2o.s2o_build_index(p, scores, idx, ws_sort)
     dsq = float((out_dense.float() ** 2).mean())
-    sweep = []
-    taus = [args.tau] if args.tau is not None else sorted(w.taus, reverse=True)
-    for tau in taus:
-        s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
-        mse = float(((out.float() - out_dense.float()) ** 2).mean())
-        density = float(exec_tiles.sum()) / dense_tiles
-        sweep.append({"tau": tau, "density": round(density, 4), "mse": mse, "rel_mse": mse / dsq})
-        log(f"tau {tau:g}: density {density:.4f} mse {mse:.3e}")
-    ok = [s for s in sweep if s["mse"] <= MSE_BUDGET]
-    chosen = max(ok, key=lambda s: s["tau"]) if ok else min(sweep, key=lambda s: s["tau"])
-    tau = chosen["tau"]
+
+    def run_mode(lists, steps, warmup, tau_fixed):
+        """tau sweep (untimed), then `steps` timed steps of score -> build_index -> attention."""
+        p = s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0, w.seg_len,
+                        w.tile_m, w.tile_n, w.scale, lists=lists)
+        n_list = s2o.list_entries(p)
+        scores = torch.empty(max(n_list, 1), dtype=torch.float32, device="cuda")
+        idx = torch.empty(max(n_list, 1), dtype=torch.int32, device="cuda")
+        ws_score = torch.empty(max(s2o.score_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+        ws_sort = torch.empty(max(s2o.build_index_workspace_bytes(p), 1), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+        exec_tiles = torch.empty((w.B, w.Hq, T), dtype=torch.int32, device="cuda")
+        s2o.s2o_score(p, q, k, scores, ws_score)
+        s2o.s2o_build_index(p, scores, idx, ws_sort)
+        sweep = []
+        taus = [tau_fixed] if tau_fixed is not None else sorted(w.taus, reverse=True)
+        for tau in taus:
+            s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
+            mse = float(((out.float() - out_dense.float()) ** 2).mean())
+            density = float(exec_tiles.sum()) / dense_tiles
+            sweep.append({"tau": tau, "density": round(density, 4), "mse": mse, "rel_mse": mse / dsq})
+            log(f"[{lists} lists] tau {tau:g}: density {density:.4f} mse {mse:.3e}")
+        ok = [r for r in sweep if r["mse"] <= MSE_BUDGET]
+        chosen = max(ok, key=lambda r: r["tau"]) if ok else min(sweep, key=lambda r: r["tau"])
+        tau = chosen["tau"]
+        for _ in range(warmup):
+            s2o.s2o_score(p, q, k, scores, ws_score)
+            s2o.s2o_build_index(p, scores, idx, ws_sort)
+            s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            ev[i][0].record(stream)
+            s2o.s2o_score(p, q, k, scores, ws_score)
+            ev[i][1].record(stream)
+            s2o.s2o_build_index(p, scores, idx, ws_sort)
+            ev[i][2].record(stream)
+            s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
+            ev[i][3].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(end) / steps
+        ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])
+        score_ms, sort_ms, attn_ms = (float(np.mean(ph[:, j])) for j in range(3))
+        executed = int(exec_tiles.sum())
+        achieved = executed * flop_per_tile / (attn_ms * 1e-3) / 1e12
+        log(f"[{lists} lists] step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index "
+            f"{sort_ms:.2f} + attn {attn_ms:.2f}")
+        res = {"tau": tau, "ms_per_step": ms_per_step, "score_ms": score_ms, "sort_ms": sort_ms,
+               "attn_ms": attn_ms, "executed": executed, "density": executed / dense_tiles,
+               "mse": chosen["mse"], "rel_mse": chosen["rel_mse"], "achieved": achieved,
+               "sweep": sweep, "exec_tiles": exec_tiles.cpu().numpy()}
+        del scores, idx, ws_score, ws_sort, out, exec_tiles
+        torch.cuda.empty_cache()
+        return res
 
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written; its FETCH_SIZE and
@@ -174,65 +211,50 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # timed steps
-    for _ in range(args.warmup):
-        step(tau)
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        s2o.s2o_score(p, q, k, scores, ws_score)
-        ev[i][1].record(stream)
-        s2o.s2o_build_index(p, scores, idx, ws_sort)
-        ev[i][2].record(stream)
-        s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
-        ev[i][3].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])
-    score_ms, sort_ms, attn_ms = (float(np.mean(ph[:, j])) for j in range(3))
-    executed = int(exec_tiles.sum())
-    attn_flops = executed * flop_per_tile
-    achieved = attn_flops / (attn_ms * 1e-3) / 1e12
-    density = executed / dense_tiles
-    log(f"step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index {sort_ms:.2f} + "
-        f"attn {attn_ms:.2f}; wall {wall:.2f} s")
+    main = run_mode("tile", args.steps, args.warmup, args.tau)
+    seg = None if args.tile_lists_only else run_mode("segment", args.steps, args.warmup, args.tau)
 
     rec = {
-        "metric": METRIC, "value": round(ms_per_step, 3), "unit": "ms", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "metric": METRIC, "value": round(main["ms_per_step"], 3), "unit": "ms", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main["ms_per_step"], 3),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded; stripes, sinks and a local band planted per KV group)",
         "config": {"workload": w.name, "batch": w.B, "heads_q": w.Hq, "heads_kv": w.Hkv,
                    "seq_len": w.N, "head_dim": w.d, "tile": [w.tile_m, w.tile_n],
-                   "seg_len": w.seg_len, "tau": tau, "parallelism": "single GPU"},
-        "phases_ms": {"s2o_score": round(score_ms, 3), "s2o_build_index": round(sort_ms, 3),
-                      "s2o_attn_fwd": round(attn_ms, 3)},
+                   "seg_len": w.seg_len, "lists": "per query tile", "tau": main["tau"],
+                   "parallelism": "single GPU"},
+        "phases_ms": {"s2o_score": round(main["score_ms"], 3),
+                      "s2o_build_index": round(main["sort_ms"], 3),
+                      "s2o_attn_fwd": round(main["attn_ms"], 3)},
         "dense_attn_fwd_ms": round(dense_ms, 3),
-        "speedup_vs_dense": round(dense_ms / ms_per_step, 3),
-        "attn_speedup_vs_dense": round(dense_ms / attn_ms, 3),
-        "density": round(density, 4), "mse_vs_dense": chosen["mse"],
-        "rel_mse_vs_dense": chosen["rel_mse"],
-        "mfma_pct_executed_tiles": round(100.0 * achieved / BF16_MFMA_PEAK_TFLOPS, 2),
-        "effective_tflops_executed_tiles": round(achieved, 1),
+        "speedup_vs_dense": round(dense_ms / main["ms_per_step"], 3),
+        "attn_speedup_vs_dense": round(dense_ms / main["attn_ms"], 3),
+        "density": round(main["density"], 4), "mse_vs_dense": main["mse"],
+        "rel_mse_vs_dense": main["rel_mse"],
+        "mfma_pct_executed_tiles": round(100.0 * main["achieved"] / BF16_MFMA_PEAK_TFLOPS, 2),
+        "effective_tflops_executed_tiles": round(main["achieved"], 1),
         "dense_tflops": round(dense_tiles * flop_per_tile / (dense_ms * 1e-3) / 1e12, 1),
-        "tau_sweep": sweep,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1),
+        "tau_sweep": main["sweep"],
+        "roofline": {"bound": "mfma", "achieved": round(main["achieved"], 1),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "frac": round(main["achieved"] / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_figure(), "kernel": "s2o_attn_fwd",
-                     "work": f"{executed} executed 128x64 tiles x {flop_per_tile:.0f} flop"},
+                     "work": f"{main['executed']} executed 128x64 tiles x {flop_per_tile:.0f} flop"},
     }
+    if seg is not None:
+        rec["segment_lists"] = {
+            "ms_per_step": round(seg["ms_per_step"], 3), "tau": seg["tau"],
+            "phases_ms": {"s2o_score": round(seg["score_ms"], 3),
+                          "s2o_build_index": round(seg["sort_ms"], 3),
+                          "s2o_attn_fwd": round(seg["attn_ms"], 3)},
+            "speedup_vs_dense": round(dense_ms / seg["ms_per_step"], 3),
+            "density": round(seg["density"], 4), "mse_vs_dense": seg["mse"],
+            "rel_mse_vs_dense": seg["rel_mse"],
+            "mfma_pct_executed_tiles": round(100.0 * seg["achieved"] / BF16_MFMA_PEAK_TFLOPS, 2),
+            "tau_sweep": seg["sweep"]}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
-        rec["cpu_baseline"] = cpu_baseline(w, x, tau, exec_tiles.cpu().numpy(), args.cpu_tiles)
+        rec["cpu_baseline"] = cpu_baseline(w, x, main["tau"], main["exec_tiles"], args.cpu_tiles)
     print(json.dumps(rec), flush=True)
 
 

@@ -79,7 +79,7 @@ def _llama8b(name, N, seg_len, taus, structure, seed):
                     seed=seed)
 
 
-TAU_SWEEP = (1e-1, 3e-2, 1e-2, 5e-3, 3e-3, 2e-3, 1e-3, 5e-4, 3e-4, 1e-4, 0.0)
+TAU_SWEEP = (1e-1, 3e-2, 1e-2, 5e-3, 3e-3, 2e-3, 1.5e-3, 1.2e-3, 1e-3, 7e-4, 5e-4, 3e-4, 1e-4, 0.0)
 
 WORKLOADS: Dict[str, Workload] = {
     # one fp32 head, 2048 tokens; the whole sequence is one segment (dense)

@@ -20,9 +20,14 @@ def short(name: str) -> str:
         if key in name:
             tail = name.split(key, 1)[1]
             if key == "attn_kernel":
-                return "s2o_attn_fwd (S2O schedule)" if "ELb1E" in tail else "dense_attn_fwd"
+                s2o = "ELb1E" in tail or ", true>" in tail
+                return "s2o_attn_fwd (S2O schedule)" if s2o else "dense_attn_fwd"
             if key in ("hist_kernel", "scatter_kernel"):
                 return key + tail.split("(")[0]
+            if key == "score_kernel":
+                return "score_kernel (s2o_score)"
+            if key == "pool_kernel":
+                return "pool_kernel (s2o_score)"
             return key
     return name[:60]
 

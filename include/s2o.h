@@ -123,10 +123,11 @@ size_t s2o_build_index_workspace_bytes(const s2o_problem *p);
 /* Index build ([GIST] KV_perm: the resulting indices form a global logical map
  * that puts likely vertical and slash stripes first).  For every list, idx
  * receives the positions [0, history length) sorted by score descending, ties
- * broken by the lower position; -0.0 and +0.0 tie.  A segmented stable radix
- * sort.
- *   scores: device fp32 [s2o_list_entries] (from s2o_score).
- *   idx: device int32 [s2o_list_entries].
+ * broken by the lower position; -0.0 and +0.0 tie.  A segmented stable sort
+ * (one bucketing pass between each list's minimum and maximum score, then a
+ * radix sort of each bucket range).
+ *   scores: device fp32 [s2o_list_entries] (from s2o_score), 16-byte aligned.
+ *   idx: device int32 [s2o_list_entries], 16-byte aligned.
  *   workspace: device, >= s2o_build_index_workspace_bytes, 256-byte aligned.
  * Errors: INVALID_ARG, UNSUPPORTED (causal = 0), WORKSPACE, HIP. */
 s2o_status s2o_build_index(const s2o_problem *p, const float *scores, int32_t *idx,

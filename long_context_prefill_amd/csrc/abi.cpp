@@ -145,7 +145,8 @@ s2o_status s2o_build_index(const s2o_problem *p, const float *scores, int32_t *i
     s2o_status st = make_geometry(p, g);
     if (st != S2O_OK) return st;
     if (!g.causal) return S2O_ERR_UNSUPPORTED;
-    if (g.list_entries > 0 && (!scores || !idx)) return S2O_ERR_INVALID_ARG;
+    if (g.list_entries > 0 && (!scores || !idx || !aligned16(scores) || !aligned16(idx)))
+        return S2O_ERR_INVALID_ARG;
     if (!workspace_ok(workspace, workspace_bytes, s2o::sort_workspace_bytes(g))) return S2O_ERR_WORKSPACE;
     if (g.list_entries == 0) return S2O_OK;
     return launch_status(s2o::launch_sort(g, scores, idx, workspace, reinterpret_cast<hipStream_t>(stream)));

@@ -1,30 +1,50 @@
-// Segmented stable LSD radix sort for the per-tile index lists, gfx950.
+// Segmented stable sort of the index lists, gfx950.
 //
 // "S2O: Early Stopping for Sparse Attention via Online Permutation",
 // gist.science technical summary, "Classement par Segment" (KV_perm): the
-// history keys of each tile are ordered by their score; the indices form the
+// history keys of each list are ordered by their score; the indices form the
 // logical map the attention kernel follows.  Order: score descending, ties to
-// the lower position (LSD radix passes are stable and start from ascending
-// positions).  -0.0 is folded onto +0.0 so the two tie.
+// the lower position.  -0.0 is folded onto +0.0 so the two tie.
 //
 // Every list is a multiple of the segment length S long and starts at a
 // multiple of S, so the concatenated lists split into equal blocks of E
-// elements (E = largest power of two dividing S, at most 4096) that never
-// straddle two lists.  Four 8-bit passes, each:
-//   hist    per block: digit histogram (wave-level multisplit, LDS counters)
-//   scan    per list: for every digit, where each block's run starts
-//   scatter per block: stable rank of every element within its digit, staged
-//           sorted in LDS, then written out in order (runs are contiguous)
-// Pass 0 reads the scores directly (key transform on the fly, positions
-// implicit); pass 3 writes only the positions, into idx.
+// entries (E = largest power of two dividing S, at most 4096) that never
+// straddle two lists.  Two data passes instead of four LSD passes:
+//
+//   1. bucket pass (one stable MSD step).  Each list's scores are split into
+//      256 buckets of equal width between the list's minimum and maximum,
+//      highest values first.  The bucket function is monotone in the score,
+//      so every bucket holds a contiguous range of the final order, and equal
+//      scores share a bucket.  minmax (per block) -> hist (per block, LDS
+//      atomics) -> scan (per list) -> scatter (per block: stable rank by a
+//      wave-level multisplit, staged in LDS, written as contiguous bucket
+//      runs of (key, position) pairs).  Within a bucket, positions ascend.
+//   2. range sort.  Each workgroup owns the buckets that start inside its
+//      chunk of C output positions, i.e. a contiguous range of the list, and
+//      sorts it by key with stable 8-bit LSD passes held in LDS.  Keys are
+//      taken relative to the range's minimum and only the bytes that differ
+//      inside the range get a pass (typically three).  Stability and the
+//      ascending positions left by pass 1 give ties to the lower position.
+//      A range larger than the LDS capacity (heavily repeated or clustered
+//      scores) is queued and sorted afterwards by one workgroup with LSD
+//      passes through global scratch, chunk by chunk in order: slower, exact.
 #include "s2o_internal.h"
+
+#include <math.h>
 
 namespace s2o {
 namespace {
 
-constexpr int RADIX = 256;
-constexpr int SORT_THREADS = 256;
-constexpr int MAX_BLOCK = 4096;
+constexpr int NB = 256;        // buckets of pass 1 = radix of the LSD passes
+constexpr int THREADS = 256;
+constexpr int NWAVES = THREADS / 64;
+constexpr int MAX_BLOCK = 4096;  // entries per pass-1 block
+constexpr int MAX_CHUNK = 2048;  // output positions owned by a range-sort workgroup
+constexpr int CAP = 4096;        // entries a range-sort workgroup holds in LDS
+constexpr int CAP_ROUNDS = CAP / THREADS;
+constexpr int OVERFLOW_GRID = 1024;  // workgroups draining the overflow queue
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // fp32 -> uint32 whose ascending order is descending score order
 __device__ inline uint32_t desc_key(float f) {
@@ -34,9 +54,7 @@ __device__ inline uint32_t desc_key(float f) {
     return ~asc;
 }
 
-__device__ inline uint64_t lanemask_lt() {
-    return (1ull << (threadIdx.x & 63)) - 1ull;
-}
+__device__ inline uint64_t lanemask_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
 
 // Lanes of the wave holding the same 8-bit digit as this lane.
 __device__ inline uint64_t match_digit(uint32_t digit) {
@@ -49,162 +67,493 @@ __device__ inline uint64_t match_digit(uint32_t digit) {
     return peers;
 }
 
-// Block geometry: E elements, NWV waves, ROUNDS rounds of 64 per wave.  Wave
-// w owns elements [w*E/NWV, (w+1)*E/NWV); round r, lane l holds element
-// w*E/NWV + 64*r + l, so block order == (wave, round, lane) order.
-template <int E>
-struct BlockCfg {
-    static constexpr int NWV = E >= 256 ? 4 : E / 64;
-    static constexpr int ROUNDS = E / (64 * NWV);
-    static_assert(E % 64 == 0 && ROUNDS >= 1, "block size");
-};
-
-template <int E, bool FIRST>
-__global__ __launch_bounds__(SORT_THREADS) void hist_kernel(const void *__restrict__ keys_in,
-                                                            int32_t *__restrict__ hist, int shift) {
-    using BC = BlockCfg<E>;
-    __shared__ int cnt[4][RADIX];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < 4 * RADIX; i += SORT_THREADS) (&cnt[0][0])[i] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * E;
-    if (wave < BC::NWV) {
-        for (int r = 0; r < BC::ROUNDS; ++r) {
-            int64_t e = base + (int64_t)wave * (E / BC::NWV) + 64 * r + lane;
-            uint32_t key = FIRST ? desc_key(reinterpret_cast<const float *>(keys_in)[e])
-                                 : reinterpret_cast<const uint32_t *>(keys_in)[e];
-            uint32_t digit = (key >> shift) & 0xFFu;
-            uint64_t peers = match_digit(digit);
-            if ((peers & lanemask_lt()) == 0) cnt[wave][digit] += __popcll(peers);
-        }
-    }
-    __syncthreads();
-    for (int v = tid; v < RADIX; v += SORT_THREADS)
-        hist[(int64_t)blockIdx.x * RADIX + v] = cnt[0][v] + cnt[1][v] + cnt[2][v] + cnt[3][v];
-}
-
-// One workgroup per list.  Turns the block histograms of the list
-// into the start of each block's digit run, relative to the block's first
-// element: hist[bb][v] = (list_off + sum_{v'<v} total[v'] + sum_{bb'<bb} hist[bb'][v]) - bb*E.
-// The first pass also records each block's offset inside its list.
-__global__ __launch_bounds__(RADIX) void scan_kernel(int32_t *__restrict__ hist,
-                                                     int32_t *__restrict__ blk_pos, Geometry g,
-                                                     int E, int first) {
-    __shared__ int tot[RADIX];
-    const int U = lists_per_head(g);
-    const int t = list_owner(g, blockIdx.x % U);
-    const int64_t bh = blockIdx.x / U;
-    const int64_t len = seg_start(g, t);
-    if (len == 0) return;
-    const int b = (int)(bh / g.Hq), h = (int)(bh % g.Hq);
-    const int64_t off = list_offset(g, b, h, t);
-    const int64_t b0 = off / E, nb = len / E;
-    const int v = threadIdx.x;
-    int run = 0;
-    for (int64_t bb = b0; bb < b0 + nb; ++bb) {
-        int c = hist[bb * RADIX + v];
-        hist[bb * RADIX + v] = run;
-        run += c;
-    }
-    tot[v] = run;
-    __syncthreads();
-    // exclusive scan over digits (Hillis-Steele on 256 entries)
-    for (int d = 1; d < RADIX; d <<= 1) {
-        int x = v >= d ? tot[v - d] : 0;
-        __syncthreads();
-        tot[v] += x;
-        __syncthreads();
-    }
-    const int digit_base = tot[v] - run;  // exclusive
-    for (int64_t bb = b0; bb < b0 + nb; ++bb)
-        hist[bb * RADIX + v] += (int)(digit_base + off - bb * E);
-    if (first && v == 0)
-        for (int64_t bb = b0; bb < b0 + nb; ++bb) blk_pos[bb] = (int32_t)(bb * E - off);
-}
-
-template <int E, bool FIRST, bool LAST>
-__global__ __launch_bounds__(SORT_THREADS) void scatter_kernel(
-    const void *__restrict__ keys_in, const int32_t *__restrict__ vals_in,
-    uint32_t *__restrict__ keys_out, int32_t *__restrict__ vals_out,
-    const int32_t *__restrict__ hist, const int32_t *__restrict__ blk_pos, int shift) {
-    using BC = BlockCfg<E>;
-    __shared__ int cnt[4][RADIX];       // per-wave digit counters, then wave offsets
-    __shared__ int dstart[RADIX];       // first sorted position of each digit in the block
-    __shared__ int dglob[RADIX];        // global run start of each digit (relative)
-    __shared__ uint32_t skey[E];
-    __shared__ int32_t sval[E];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < 4 * RADIX; i += SORT_THREADS) (&cnt[0][0])[i] = 0;
-    const int64_t base = (int64_t)blockIdx.x * E;
-    for (int v = tid; v < RADIX; v += SORT_THREADS) dglob[v] = hist[(int64_t)blockIdx.x * RADIX + v];
-    __syncthreads();
-
-    uint32_t key[BC::ROUNDS];
-    int32_t val[BC::ROUNDS];
-    int rank[BC::ROUNDS];
-    if (wave < BC::NWV) {
-        const int32_t pos0 = FIRST ? blk_pos[blockIdx.x] : 0;
-#pragma unroll
-        for (int r = 0; r < BC::ROUNDS; ++r) {
-            const int local = wave * (E / BC::NWV) + 64 * r + lane;
-            const int64_t e = base + local;
-            if (FIRST) {
-                key[r] = desc_key(reinterpret_cast<const float *>(keys_in)[e]);
-                val[r] = pos0 + local;
-            } else {
-                key[r] = reinterpret_cast<const uint32_t *>(keys_in)[e];
-                val[r] = vals_in[e];
-            }
-            const uint32_t digit = (key[r] >> shift) & 0xFFu;
-            const uint64_t peers = match_digit(digit);
-            const int before = cnt[wave][digit];  // read by all peers before the leader updates
-            rank[r] = before + __popcll(peers & lanemask_lt());
-            if ((peers & lanemask_lt()) == 0) cnt[wave][digit] = before + __popcll(peers);
-        }
-    }
-    __syncthreads();
-    // per digit: exclusive offsets of the waves, and the digit's start in the block
-    for (int v = tid; v < RADIX; v += SORT_THREADS) {
-        int s = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            int c = cnt[w][v];
-            cnt[w][v] = s;
-            s += c;
-        }
-        dstart[v] = s;  // total for now
-    }
-    __syncthreads();
-    if (tid < 64) {  // exclusive scan of the 256 digit totals by one wave
-        int a0 = dstart[4 * tid], a1 = dstart[4 * tid + 1], a2 = dstart[4 * tid + 2], a3 = dstart[4 * tid + 3];
+// Exclusive scan of 256 ints in LDS, in place, by the first wave; the totals'
+// sum is returned to that wave.  Callers synchronise around it.
+__device__ inline void scan256(int *v) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        int a0 = v[4 * lane], a1 = v[4 * lane + 1], a2 = v[4 * lane + 2], a3 = v[4 * lane + 3];
         int sum = a0 + a1 + a2 + a3, incl = sum;
+#pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             int x = __shfl_up(incl, d);
             if (lane >= d) incl += x;
         }
         int ex = incl - sum;
-        dstart[4 * tid] = ex;
-        dstart[4 * tid + 1] = ex + a0;
-        dstart[4 * tid + 2] = ex + a0 + a1;
-        dstart[4 * tid + 3] = ex + a0 + a1 + a2;
+        v[4 * lane] = ex;
+        v[4 * lane + 1] = ex + a0;
+        v[4 * lane + 2] = ex + a0 + a1;
+        v[4 * lane + 3] = ex + a0 + a1 + a2;
     }
-    __syncthreads();
-    if (wave < BC::NWV) {
+}
+
+// A list: global list id -> its offset and length in the concatenated layout.
+struct ListRef {
+    int64_t off, len;
+};
+__device__ inline ListRef list_ref(const Geometry &g, int lid) {
+    const int U = lists_per_head(g);
+    const int bh = lid / U, t = list_owner(g, lid % U);
+    return {list_offset(g, bh / g.Hq, bh % g.Hq, t), seg_start(g, t)};
+}
+
+// Bucket function of pass 1: NB buckets of equal width over [lo, hi], the
+// highest scores in digit 0.  Non-increasing in x, so buckets never interleave.
+struct Buckets {
+    float lo, sc;  // sc = 0: a single bucket
+};
+__device__ inline uint32_t bucket_digit(float x, Buckets r) {
+    if (!(r.sc > 0.f)) return NB - 1;
+    const float f = (x - r.lo) * r.sc;  // in [0, NB(1+eps)] since lo <= x <= hi
+    int b = (int)f;
+    b = b < NB - 1 ? b : NB - 1;
+    return (uint32_t)(NB - 1 - b);
+}
+
+// Bucket parameters of the list owning block `blk` (every thread gets them).
+// The reduction order is fixed, so hist and scatter agree bit for bit.
+__device__ Buckets list_buckets(const Geometry &g, const int32_t *blk_list, const float *blk_mm,
+                                int E, float *sh) {
+    const ListRef L = list_ref(g, blk_list[blockIdx.x]);
+    const int64_t b0 = L.off / E, nb = L.len / E;
+    if (threadIdx.x < 64) {
+        float lo = INFINITY, hi = -INFINITY;
+        for (int64_t i = threadIdx.x; i < nb; i += 64) {
+            lo = fminf(lo, blk_mm[2 * (b0 + i)]);
+            hi = fmaxf(hi, blk_mm[2 * (b0 + i) + 1]);
+        }
 #pragma unroll
-        for (int r = 0; r < BC::ROUNDS; ++r) {
-            const uint32_t digit = (key[r] >> shift) & 0xFFu;
-            const int p = dstart[digit] + cnt[wave][digit] + rank[r];
-            skey[p] = key[r];
-            sval[p] = val[r];
+        for (int o = 32; o > 0; o >>= 1) {
+            lo = fminf(lo, __shfl_xor(lo, o));
+            hi = fmaxf(hi, __shfl_xor(hi, o));
+        }
+        if (threadIdx.x == 0) {
+            sh[0] = lo;
+            sh[1] = hi;
         }
     }
     __syncthreads();
-    for (int i = tid; i < E; i += SORT_THREADS) {
-        const uint32_t k = skey[i];
-        const uint32_t digit = (k >> shift) & 0xFFu;
-        const int64_t dst = base + dglob[digit] + (i - dstart[digit]);
-        if (!LAST) keys_out[dst] = k;
-        vals_out[dst] = sval[i];
+    const float lo = sh[0], d = sh[1] - lo;
+    float sc = d > 0.f ? (float)NB / d : 0.f;
+    if (!(sc < INFINITY)) sc = 0.f;  // d overflowed or is denormal-small
+    return {lo, sc};
+}
+
+// One workgroup per list: records which list every block belongs to, and
+// empties the overflow queue.
+__global__ __launch_bounds__(THREADS) void plan_kernel(int32_t *__restrict__ blk_list,
+                                                       int32_t *__restrict__ queue_len, Geometry g, int E) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *queue_len = 0;
+    const ListRef L = list_ref(g, blockIdx.x);
+    const int64_t b0 = L.off / E, nb = L.len / E;
+    for (int64_t i = threadIdx.x; i < nb; i += THREADS) blk_list[b0 + i] = (int32_t)blockIdx.x;
+}
+
+// Per block: minimum and maximum score.
+__global__ __launch_bounds__(THREADS) void minmax_kernel(const float *__restrict__ scores,
+                                                         float *__restrict__ blk_mm, int E) {
+    __shared__ float red[2][NWAVES];
+    const float *s = scores + (int64_t)blockIdx.x * E;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int i = 4 * threadIdx.x; i < E; i += 4 * THREADS) {
+        const float4 x = *reinterpret_cast<const float4 *>(s + i);
+        lo = fminf(fminf(lo, x.x), fminf(x.y, fminf(x.z, x.w)));
+        hi = fmaxf(fmaxf(hi, x.x), fmaxf(x.y, fmaxf(x.z, x.w)));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, o));
+        hi = fmaxf(hi, __shfl_xor(hi, o));
+    }
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        red[0][wave] = lo;
+        red[1][wave] = hi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < NWAVES; ++w) {
+            lo = fminf(lo, red[0][w]);
+            hi = fmaxf(hi, red[1][w]);
+        }
+        blk_mm[2 * blockIdx.x] = lo;
+        blk_mm[2 * blockIdx.x + 1] = hi;
+    }
+}
+
+// Per block: bucket histogram (order-free, so LDS atomics).
+__global__ __launch_bounds__(THREADS) void hist_kernel(const float *__restrict__ scores,
+                                                       const int32_t *__restrict__ blk_list,
+                                                       const float *__restrict__ blk_mm,
+                                                       int32_t *__restrict__ hist, Geometry g, int E) {
+    __shared__ int cnt[NWAVES][NB];
+    __shared__ float sh[2];
+    for (int i = threadIdx.x; i < NWAVES * NB; i += THREADS) (&cnt[0][0])[i] = 0;
+    const Buckets bk = list_buckets(g, blk_list, blk_mm, E, sh);  // synchronises
+    const int wave = threadIdx.x >> 6;
+    const float *s = scores + (int64_t)blockIdx.x * E;
+    for (int i = 4 * threadIdx.x; i < E; i += 4 * THREADS) {
+        const float4 x = *reinterpret_cast<const float4 *>(s + i);
+        atomicAdd(&cnt[wave][bucket_digit(x.x, bk)], 1);
+        atomicAdd(&cnt[wave][bucket_digit(x.y, bk)], 1);
+        atomicAdd(&cnt[wave][bucket_digit(x.z, bk)], 1);
+        atomicAdd(&cnt[wave][bucket_digit(x.w, bk)], 1);
+    }
+    __syncthreads();
+    for (int v = threadIdx.x; v < NB; v += THREADS) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) c += cnt[w][v];
+        hist[(int64_t)blockIdx.x * NB + v] = c;
+    }
+}
+
+// One workgroup (NB threads) per list.  Turns the block histograms into the
+// start of each block's bucket run relative to the block's first entry,
+//   hist[bb][v] = off + base[v] + sum_{bb' < bb} count[bb'][v] - bb*E,
+// and records the list's bucket starts base[0..NB) and its length.
+__global__ __launch_bounds__(NB) void scan_kernel(int32_t *__restrict__ hist, int32_t *__restrict__ bstart,
+                                                  Geometry g, int E) {
+    __shared__ int tot[NB];
+    const ListRef L = list_ref(g, blockIdx.x);
+    if (L.len == 0) return;
+    const int64_t b0 = L.off / E, nb = L.len / E;
+    const int v = threadIdx.x;
+    int run = 0;
+    for (int64_t bb = b0; bb < b0 + nb; ++bb) {
+        const int c = hist[bb * NB + v];
+        hist[bb * NB + v] = run;
+        run += c;
+    }
+    tot[v] = run;
+    __syncthreads();
+    scan256(tot);
+    __syncthreads();
+    const int base = tot[v];
+    for (int64_t bb = b0; bb < b0 + nb; ++bb) hist[bb * NB + v] += (int)(base + L.off - bb * E);
+    int32_t *bs = bstart + (int64_t)blockIdx.x * (NB + 1);
+    bs[v] = base;
+    if (v == 0) bs[NB] = (int32_t)L.len;
+}
+
+// Per block: stable scatter into bucket runs of (key, position) pairs.
+template <int E>
+__global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restrict__ scores,
+                                                          const int32_t *__restrict__ blk_list,
+                                                          const float *__restrict__ blk_mm,
+                                                          const int32_t *__restrict__ hist,
+                                                          u32x2 *__restrict__ pairs, Geometry g) {
+    constexpr int NWV = E >= 256 ? NWAVES : E / 64;  // waves holding entries
+    constexpr int ROUNDS = E / (64 * NWV);           // wave w owns [w*E/NWV, (w+1)*E/NWV)
+    __shared__ int cnt[NWAVES][NB];  // per-wave digit counters, then wave offsets
+    __shared__ int dstart[NB];       // first staged position of each digit
+    __shared__ int dglob[NB];        // run start of each digit, relative to the block
+    __shared__ uint32_t skey[E];
+    __shared__ int32_t spos[E];
+    __shared__ uint8_t sdig[E];
+    __shared__ float sh[2];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < NWAVES * NB; i += THREADS) (&cnt[0][0])[i] = 0;
+    for (int v = tid; v < NB; v += THREADS) dglob[v] = hist[(int64_t)blockIdx.x * NB + v];
+    const Buckets bk = list_buckets(g, blk_list, blk_mm, E, sh);  // synchronises
+    const int64_t base = (int64_t)blockIdx.x * E;
+    const int32_t pos0 = (int32_t)(base - list_ref(g, blk_list[blockIdx.x]).off);
+
+    float x[ROUNDS];
+    uint32_t dig[ROUNDS];
+    int rank[ROUNDS];
+    if (wave < NWV) {
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) x[r] = scores[base + wave * (E / NWV) + 64 * r + lane];
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            dig[r] = bucket_digit(x[r], bk);
+            const uint64_t peers = match_digit(dig[r]);
+            const int before = cnt[wave][dig[r]];  // read by all peers before the leader updates
+            rank[r] = before + __popcll(peers & lanemask_lt());
+            if ((peers & lanemask_lt()) == 0) cnt[wave][dig[r]] = before + __popcll(peers);
+        }
+    }
+    __syncthreads();
+    for (int v = tid; v < NB; v += THREADS) {
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) {
+            const int c = cnt[w][v];
+            cnt[w][v] = s;
+            s += c;
+        }
+        dstart[v] = s;
+    }
+    __syncthreads();
+    scan256(dstart);
+    __syncthreads();
+    if (wave < NWV) {
+#pragma unroll
+        for (int r = 0; r < ROUNDS; ++r) {
+            const int p = dstart[dig[r]] + cnt[wave][dig[r]] + rank[r];
+            skey[p] = desc_key(x[r]);
+            spos[p] = pos0 + wave * (E / NWV) + 64 * r + lane;
+            sdig[p] = (uint8_t)dig[r];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < E; i += THREADS) {
+        const int d = sdig[i];
+        u32x2 pr;
+        pr.x = skey[i];
+        pr.y = (uint32_t)spos[i];
+        pairs[base + dglob[d] + (i - dstart[d])] = pr;
+    }
+}
+
+// Stable rank of one chunk (striped: entry w*rounds*64 + r*64 + lane) by the
+// digit (rel >> shift) & 0xFF, over the first `rounds` of the R register
+// rounds.  On return cnt[w][d] holds the offset of wave w's run inside digit
+// d's run of the chunk and dtot[d] the chunk's count of d; an entry's position
+// inside its digit run is cnt[w][d] + rank[r].
+template <int R>
+__device__ __forceinline__ void rank_chunk(const uint32_t (&rel)[R], int (&rank)[R], int rounds, int shift,
+                                  int (*cnt)[NB], int *dtot) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    for (int i = tid; i < NWAVES * NB; i += THREADS) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < rounds) {
+            const uint32_t d = (rel[r] >> shift) & 0xFFu;
+            const uint64_t peers = match_digit(d);
+            const int before = cnt[wave][d];
+            rank[r] = before + __popcll(peers & lanemask_lt());
+            if ((peers & lanemask_lt()) == 0) cnt[wave][d] = before + __popcll(peers);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one round at a time: bounds register use
+    }
+    __syncthreads();
+    for (int v = tid; v < NB; v += THREADS) {
+        int s = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) {
+            const int c = cnt[w][v];
+            cnt[w][v] = s;
+            s += c;
+        }
+        dtot[v] = s;
+    }
+    __syncthreads();
+}
+
+// Block-wide reductions (every thread gets the result).
+__device__ inline uint32_t block_min(uint32_t x, uint32_t *sh) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    uint32_t r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) r = min(r, sh[w]);
+    return r;
+}
+__device__ inline uint32_t block_or(uint32_t x, uint32_t *sh) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x |= (uint32_t)__shfl_xor((int)x, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    uint32_t r = sh[0];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) r |= sh[w];
+    return r;
+}
+
+// Sorts the m <= R*THREADS entries of one range in LDS and writes their
+// positions: stable 8-bit LSD passes on the key relative to the range minimum,
+// only over the bytes that vary.  Padding entries (rel = all ones) stay last.
+template <int R>
+__device__ __forceinline__ void sort_in_lds(const u32x2 *__restrict__ in, int32_t *__restrict__ out, int m, uint32_t *skey,
+                            int32_t *spos, int (*cnt)[NB], int *dtot, uint32_t *red) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wbase = wave * R * 64 + lane;
+    uint32_t rel[R];
+    int32_t pos[R];
+    int rank[R];
+    uint32_t kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = wbase + 64 * r;
+        u32x2 pr;
+        pr.x = 0xFFFFFFFFu;
+        pr.y = 0;
+        if (i < m) pr = in[i];
+        rel[r] = pr.x;
+        pos[r] = (int32_t)pr.y;
+        kmin = min(kmin, pr.x);
+    }
+    kmin = block_min(kmin, red);
+    uint32_t span = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const bool real = wbase + 64 * r < m;
+        rel[r] = real ? rel[r] - kmin : 0xFFFFFFFFu;
+        span |= real ? rel[r] : 0u;
+    }
+    span = block_or(span, red);
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 8 * pass;
+        if (((span >> shift) & 0xFFu) == 0) continue;  // digit constant in the range
+        rank_chunk<R>(rel, rank, R, shift, cnt, dtot);
+        scan256(dtot);
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t d = (rel[r] >> shift) & 0xFFu;
+            const int p = dtot[d] + cnt[wave][d] + rank[r];
+            skey[p] = rel[r];
+            spos[p] = pos[r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            rel[r] = skey[wbase + 64 * r];
+            pos[r] = spos[wbase + 64 * r];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (wbase + 64 * r < m) out[wbase + 64 * r] = pos[r];
+}
+
+// An oversized range, queued for overflow_kernel.
+struct Overflow {
+    int32_t lid, rs, m;
+};
+
+// One workgroup per chunk of C output positions of a list: sorts the buckets
+// that start inside the chunk (see the file comment) and writes positions.
+// A range larger than CAP is queued for overflow_kernel instead.
+template <int C>
+__global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__restrict__ pairs,
+                                                                int32_t *__restrict__ idx,
+                                                                const int32_t *__restrict__ blk_list,
+                                                                const int32_t *__restrict__ bstart,
+                                                                Overflow *__restrict__ queue,
+                                                                int32_t *__restrict__ queue_len,
+                                                                Geometry g, int E) {
+    __shared__ uint32_t skey[CAP];
+    __shared__ int32_t spos[CAP];
+    __shared__ int cnt[NWAVES][NB];
+    __shared__ int dtot[NB];
+    __shared__ uint32_t red[NWAVES];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t e0 = (int64_t)blockIdx.x * C;
+    const int lid = blk_list[e0 / E];
+    const ListRef L = list_ref(g, lid);
+    const int32_t g0 = (int32_t)(e0 - L.off);
+    const int32_t *bs = bstart + (int64_t)lid * (NB + 1);
+    // buckets starting in [g0, g0 + C) are [lo_b, hi_b); bs[NB] = len >= g0 + C
+    const int lo_b = __syncthreads_count(bs[tid] < g0);
+    const int hi_b = __syncthreads_count(bs[tid] < g0 + C);
+    const int32_t rs = bs[lo_b], m = bs[hi_b] - rs;
+    if (m == 0) return;
+    if (m > CAP) {
+        if (tid == 0) queue[atomicAdd(queue_len, 1)] = {lid, rs, m};
+        return;
+    }
+    const u32x2 *in = pairs + L.off + rs;
+    int32_t *out = idx + L.off + rs;
+    switch ((m + THREADS - 1) / THREADS) {  // one instantiation per round count
+#define S2O_SORT_CASE(R) \
+    case R: sort_in_lds<R>(in, out, m, skey, spos, cnt, dtot, red); break;
+        S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
+        S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
+        S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
+        S2O_SORT_CASE(13) S2O_SORT_CASE(14) S2O_SORT_CASE(15) S2O_SORT_CASE(16)
+#undef S2O_SORT_CASE
+        default: break;
+    }
+}
+
+// Oversized ranges (heavily repeated or clustered scores): each workgroup
+// takes queued ranges in turn and sorts one with stable LSD passes through
+// global scratch, CAP entries at a time in order.
+__global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ pairs,
+                                                           u32x2 *__restrict__ scratch,
+                                                           int32_t *__restrict__ idx,
+                                                           const Overflow *__restrict__ queue,
+                                                           const int32_t *__restrict__ queue_len,
+                                                           Geometry g) {
+    __shared__ int cnt[NWAVES][NB];
+    __shared__ int dtot[NB];
+    __shared__ int run[NB];
+    __shared__ uint32_t red[NWAVES];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nq = *queue_len;
+    uint32_t rel[CAP_ROUNDS];
+    int32_t pos[CAP_ROUNDS];
+    int rank[CAP_ROUNDS];
+    for (int q = blockIdx.x; q < nq; q += gridDim.x) {
+        const Overflow ov = queue[q];
+        const int64_t base = list_ref(g, ov.lid).off + ov.rs;
+        const int m = ov.m;
+        u32x2 *src = pairs + base, *dst = scratch + base;
+        uint32_t kmin = 0xFFFFFFFFu;
+        for (int i = tid; i < m; i += THREADS) kmin = min(kmin, src[i].x);
+        kmin = block_min(kmin, red);
+        uint32_t span = 0;
+        for (int i = tid; i < m; i += THREADS) span |= src[i].x - kmin;
+        span = block_or(span, red);
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 8 * pass;
+            if (((span >> shift) & 0xFFu) == 0) continue;
+            for (int v = tid; v < NB; v += THREADS) run[v] = 0;
+            __syncthreads();
+            for (int i = tid; i < m; i += THREADS) atomicAdd(&run[((src[i].x - kmin) >> shift) & 0xFFu], 1);
+            __syncthreads();
+            scan256(run);
+            __syncthreads();
+            for (int c0 = 0; c0 < m; c0 += CAP) {
+                const int cm = min(CAP, m - c0);
+                const int rounds = (cm + THREADS - 1) / THREADS;
+                const int wbase = wave * rounds * 64 + lane;
+#pragma unroll
+                for (int r = 0; r < CAP_ROUNDS; ++r) {
+                    if (r < rounds) {
+                        const int i = wbase + 64 * r;
+                        if (i < cm) {
+                            const u32x2 pr = src[c0 + i];
+                            rel[r] = pr.x - kmin;
+                            pos[r] = (int32_t)pr.y;
+                        } else {
+                            rel[r] = 0xFFFFFFFFu;
+                            pos[r] = 0;
+                        }
+                    }
+                }
+                rank_chunk<CAP_ROUNDS>(rel, rank, rounds, shift, cnt, dtot);
+#pragma unroll
+                for (int r = 0; r < CAP_ROUNDS; ++r) {
+                    if (r < rounds && wbase + 64 * r < cm) {
+                        const uint32_t d = (rel[r] >> shift) & 0xFFu;
+                        u32x2 pr;
+                        pr.x = rel[r] + kmin;
+                        pr.y = (uint32_t)pos[r];
+                        dst[run[d] + cnt[wave][d] + rank[r]] = pr;
+                    }
+                }
+                __syncthreads();
+                // padding entries (rel = all ones, digit 0xFF in every pass) rank after
+                // every real entry of digit 0xFF and are neither written nor counted
+                for (int v = tid; v < NB; v += THREADS) run[v] += dtot[v] - (v == 0xFF ? rounds * THREADS - cm : 0);
+                __syncthreads();
+            }
+            u32x2 *t = src;
+            src = dst;
+            dst = t;
+        }
+        for (int i = tid; i < m; i += THREADS) idx[base + i] = (int32_t)src[i].y;
+        __syncthreads();  // the next range reuses the LDS
     }
 }
 
@@ -213,10 +562,16 @@ int block_elems(const Geometry &g) {
     return e > MAX_BLOCK ? MAX_BLOCK : e;
 }
 
+int range_chunk(const Geometry &g) {
+    const int e = block_elems(g);
+    return e < MAX_CHUNK ? e : MAX_CHUNK;
+}
+
 struct SortWs {
-    uint32_t *keys_a, *keys_b;
-    int32_t *vals_a;
-    int32_t *hist, *blk_pos;
+    u32x2 *pairs, *scratch;
+    int32_t *hist, *blk_list, *bstart, *queue_len;
+    float *blk_mm;
+    Overflow *queue;
     size_t bytes;
 };
 
@@ -225,19 +580,26 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 SortWs carve(const Geometry &g, void *base) {
     const int64_t n = g.list_entries;
     const int64_t nblocks = n / block_elems(g);
+    const int64_t lists = (int64_t)g.B * g.Hq * lists_per_head(g);
     SortWs w;
     size_t off = 0;
     char *p = reinterpret_cast<char *>(base);
-    w.keys_a = reinterpret_cast<uint32_t *>(p + off);
-    off += align256(n * 4);
-    w.keys_b = reinterpret_cast<uint32_t *>(p + off);
-    off += align256(n * 4);
-    w.vals_a = reinterpret_cast<int32_t *>(p + off);
-    off += align256(n * 4);
+    w.pairs = reinterpret_cast<u32x2 *>(p + off);
+    off += align256(n * 8);
+    w.scratch = reinterpret_cast<u32x2 *>(p + off);
+    off += align256(n * 8);
     w.hist = reinterpret_cast<int32_t *>(p + off);
-    off += align256((size_t)nblocks * RADIX * 4);
-    w.blk_pos = reinterpret_cast<int32_t *>(p + off);
+    off += align256((size_t)nblocks * NB * 4);
+    w.blk_list = reinterpret_cast<int32_t *>(p + off);
     off += align256((size_t)nblocks * 4);
+    w.blk_mm = reinterpret_cast<float *>(p + off);
+    off += align256((size_t)nblocks * 8);
+    w.bstart = reinterpret_cast<int32_t *>(p + off);
+    off += align256((size_t)lists * (NB + 1) * 4);
+    w.queue = reinterpret_cast<Overflow *>(p + off);  // at most one entry per chunk
+    off += align256((size_t)(n / range_chunk(g)) * sizeof(Overflow));
+    w.queue_len = reinterpret_cast<int32_t *>(p + off);
+    off += 256;
     w.bytes = off;
     return w;
 }
@@ -245,44 +607,21 @@ SortWs carve(const Geometry &g, void *base) {
 template <int E>
 hipError_t run_sort(const Geometry &g, const float *scores, int32_t *idx, const SortWs &w,
                     hipStream_t stream) {
+    constexpr int C = E < MAX_CHUNK ? E : MAX_CHUNK;  // = range_chunk(g)
     const int64_t nblocks = g.list_entries / E;
     const unsigned lists = (unsigned)((int64_t)g.B * g.Hq * lists_per_head(g));
-    // pass p: input keys/vals -> output keys/vals
-    //   0: scores           -> keys_a, vals_a
-    //   1: keys_a, vals_a   -> keys_b, idx      (idx doubles as scratch)
-    //   2: keys_b, idx      -> keys_a, vals_a
-    //   3: keys_a, vals_a   -> idx (positions only)
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 8 * pass;
-        const void *kin = pass == 0 ? (const void *)scores : pass == 2 ? (const void *)w.keys_b
-                                                                       : (const void *)w.keys_a;
-        const int32_t *vin = pass == 1 ? w.vals_a : pass == 2 ? idx : w.vals_a;
-        uint32_t *kout = pass == 1 ? w.keys_b : w.keys_a;
-        int32_t *vout = pass == 1 || pass == 3 ? idx : w.vals_a;
-        if (pass == 0)
-            hipLaunchKernelGGL((hist_kernel<E, true>), dim3((unsigned)nblocks), dim3(SORT_THREADS), 0,
-                               stream, kin, w.hist, shift);
-        else
-            hipLaunchKernelGGL((hist_kernel<E, false>), dim3((unsigned)nblocks), dim3(SORT_THREADS), 0,
-                               stream, kin, w.hist, shift);
-        hipLaunchKernelGGL(scan_kernel, dim3(lists), dim3(RADIX), 0, stream, w.hist, w.blk_pos, g, E,
-                           pass == 0 ? 1 : 0);
-        if (pass == 0)
-            hipLaunchKernelGGL((scatter_kernel<E, true, false>), dim3((unsigned)nblocks),
-                               dim3(SORT_THREADS), 0, stream, kin, vin, kout, vout, w.hist, w.blk_pos,
-                               shift);
-        else if (pass == 3)
-            hipLaunchKernelGGL((scatter_kernel<E, false, true>), dim3((unsigned)nblocks),
-                               dim3(SORT_THREADS), 0, stream, kin, vin, kout, vout, w.hist, w.blk_pos,
-                               shift);
-        else
-            hipLaunchKernelGGL((scatter_kernel<E, false, false>), dim3((unsigned)nblocks),
-                               dim3(SORT_THREADS), 0, stream, kin, vin, kout, vout, w.hist, w.blk_pos,
-                               shift);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    hipLaunchKernelGGL(plan_kernel, dim3(lists), dim3(THREADS), 0, stream, w.blk_list, w.queue_len, g, E);
+    hipLaunchKernelGGL(minmax_kernel, dim3((unsigned)nblocks), dim3(THREADS), 0, stream, scores, w.blk_mm, E);
+    hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nblocks), dim3(THREADS), 0, stream, scores, w.blk_list,
+                       w.blk_mm, w.hist, g, E);
+    hipLaunchKernelGGL(scan_kernel, dim3(lists), dim3(NB), 0, stream, w.hist, w.bstart, g, E);
+    hipLaunchKernelGGL(scatter_kernel<E>, dim3((unsigned)nblocks), dim3(THREADS), 0, stream, scores,
+                       w.blk_list, w.blk_mm, w.hist, w.pairs, g);
+    hipLaunchKernelGGL(range_sort_kernel<C>, dim3((unsigned)(g.list_entries / C)), dim3(THREADS), 0, stream,
+                       w.pairs, idx, w.blk_list, w.bstart, w.queue, w.queue_len, g, E);
+    hipLaunchKernelGGL(overflow_kernel, dim3(OVERFLOW_GRID), dim3(THREADS), 0, stream, w.pairs, w.scratch, idx,
+                       w.queue, w.queue_len, g);
+    return hipGetLastError();
 }
 
 }  // namespace

@@ -328,3 +328,49 @@ def test_llama8b_128k_segment_lists_sampled():
     tiles = sample_tiles(w, heads=(3, 30), n_random=8, seed=6)
     o, ex = run.attn(1e-3)
     assert_report(compare(run, tiles, 1e-3, o, ex, check_lists=True), "bf16")
+
+
+# ------------------------------------------------ index build on crafted scores --
+
+def _crafted_scores(kind, n, rng):
+    if kind == "all_equal":            # one bucket per list, every entry tied
+        return np.zeros(n, np.float32)
+    if kind == "signed_zeros":         # -0.0 and +0.0 tie
+        return np.where(rng.random(n) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    if kind == "few_values":           # large buckets full of ties
+        return rng.choice(np.array([-1.5, 0.0, 2.5, 7.0], np.float32), n)
+    if kind == "outlier":              # one huge value squeezes the rest into one bucket
+        s = rng.standard_normal(n).astype(np.float32)
+        s[rng.integers(0, n, 8)] = np.float32(1e30)
+        return s
+    if kind == "extreme_range":        # max - min overflows fp32
+        s = rng.standard_normal(n).astype(np.float32) * np.float32(1e-3)
+        s[::997] = np.float32(3e38)
+        s[::1009] = np.float32(-3e38)
+        s[::31] = np.float32(1e-40)    # denormals
+        return s
+    if kind == "gaussian_ties":        # the usual case, with exact ties mixed in
+        s = (rng.standard_normal(n) * 4).astype(np.float32)
+        s[::5] = np.round(s[::5])
+        return s
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("lists", ["tile", "segment"])
+@pytest.mark.parametrize("kind", ["all_equal", "signed_zeros", "few_values", "outlier",
+                                  "extreme_range", "gaussian_ties"])
+def test_build_index_crafted_scores(kind, lists):
+    """s2o_build_index on score arrays that force oversized buckets, exact ties,
+    signed zeros, denormals and an overflowing score range, against the oracle's
+    (score desc, position asc) order of every list."""
+    N, S, BM = 32768, 8192, 128
+    p = s2o.problem(1, 2, 1, N, 64, 1, S, BM, 64, lists=lists)
+    po = oracle.problem(1, 2, 1, N, 64, "bf16", S, BM, 64, 0.125, per_segment=(lists == "segment"))
+    n = s2o.list_entries(p)
+    assert n == oracle.list_entries(po)
+    rng = np.random.default_rng(sum(ord(c) for c in kind))
+    sc = _crafted_scores(kind, n, rng)
+    say(f"build_index crafted scores kind={kind} lists={lists} n={n}")
+    idx = s2o.s2o_build_index(p, torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), oracle.lists_all(po, sc))

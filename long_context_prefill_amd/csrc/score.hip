@@ -14,10 +14,11 @@
 // Layout of the score kernel: one workgroup per (b, KV head, segment s >= 1,
 // block of 256 history keys).  Each thread holds one key row in fp32
 // registers and runs it against every (query head of the group, tile of the
-// segment) pair.  A pair's pooled query is the same for the whole wave, so it
-// is read through the scalar cache and fed to the fmas as SGPR operands (no
-// VGPRs, which keeps three waves per SIMD).  Two pairs are kept in flight for
-// instruction-level parallelism; each chain is still evaluated in ascending k.
+// segment) pair, four pairs at a time.  A pair's pooled query is spread over
+// the 16 lanes of each row (D/16 registers per lane) and broadcast element by
+// element with DPP row_newbcast as the fma's first operand; the next four
+// pairs load while the current four compute.  Each chain is still evaluated in
+// ascending k.
 #include "s2o_internal.h"
 
 namespace s2o {
@@ -44,11 +45,14 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, floa
     const T *src = Q + (bh * g.N + (int64_t)t * g.BM) * g.d + k;
     float sum = 0.0f;
     for (int r = 0; r < g.BM; ++r) sum = sum + widen<T>(src[(int64_t)r * g.d]);
-    qbar[gid] = sum * (1.0f / (float)g.BM);  // exact: BM is a power of two
+    // stored lane-major: element k of a pooled query at (k % 16) * (d / 16) + k / 16,
+    // so a lane reads its d/16 elements (16c + lane, c = 0..) as one contiguous run
+    qbar[tile * g.d + (k & 15) * (g.d >> 4) + (k >> 4)] = sum * (1.0f / (float)g.BM);  // exact: BM = 2^n
 }
 
 // Segment representatives (per-segment lists): mean of the segment's tile
 // means, an fp32 sum over its tiles in ascending order times fl(1/tiles).
+// Elementwise, so it works in the lane-major layout unchanged.
 __global__ __launch_bounds__(256) void segpool_kernel(const float *__restrict__ qbar,
                                                       float *__restrict__ qseg, Geometry g,
                                                       int64_t total) {
@@ -66,13 +70,42 @@ __global__ __launch_bounds__(256) void segpool_kernel(const float *__restrict__ 
 }
 
 constexpr int SCORE_KEYS = 256;   // keys per workgroup (one per thread)
-constexpr int SCORE_ILP = 2;      // pairs evaluated together (independent fma chains)
+constexpr int SCORE_ILP = 4;      // pairs evaluated together (independent fma chains)
+
+// acc[p] = fma(qbar_p[16c + n], kr[16c + n], acc[p]) for n = 0..15 in ascending
+// order, for the four pairs p.  Lane i of every 16-lane row holds
+// qbar_p[16c + i] in q_p; DPP row_newbcast:n hands lane n's value to its whole
+// row, so every fma takes its pooled-query element straight from another
+// lane's register at full rate.  The four chains are interleaved, which keeps
+// three instructions between dependent ones (DPP needs two wait states after a
+// VALU write of an operand); the leading s_nop covers writes made just before.
+#define S2O_DPP_FMA(n, K)                                                                    \
+    "v_fmac_f32_dpp %0, %4, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"        \
+    "v_fmac_f32_dpp %1, %5, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"        \
+    "v_fmac_f32_dpp %2, %6, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"        \
+    "v_fmac_f32_dpp %3, %7, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"
+
+__device__ __forceinline__ void fma16x4(float &a0, float &a1, float &a2, float &a3, float q0, float q1,
+                                        float q2, float q3, const float *k) {
+    asm volatile("s_nop 1\n\t"
+                 S2O_DPP_FMA(0, "%8") S2O_DPP_FMA(1, "%9") S2O_DPP_FMA(2, "%10") S2O_DPP_FMA(3, "%11")
+                 S2O_DPP_FMA(4, "%12") S2O_DPP_FMA(5, "%13") S2O_DPP_FMA(6, "%14") S2O_DPP_FMA(7, "%15")
+                 S2O_DPP_FMA(8, "%16") S2O_DPP_FMA(9, "%17") S2O_DPP_FMA(10, "%18") S2O_DPP_FMA(11, "%19")
+                 S2O_DPP_FMA(12, "%20") S2O_DPP_FMA(13, "%21") S2O_DPP_FMA(14, "%22") S2O_DPP_FMA(15, "%23")
+                 : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
+                 : "v"(q0), "v"(q1), "v"(q2), "v"(q3), "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]),
+                   "v"(k[5]), "v"(k[6]), "v"(k[7]), "v"(k[8]), "v"(k[9]), "v"(k[10]), "v"(k[11]), "v"(k[12]),
+                   "v"(k[13]), "v"(k[14]), "v"(k[15])
+                 : "memory");  // keeps the next group's loads issued ahead of the block
+}
+#undef S2O_DPP_FMA
 
 template <typename T, int D>
 __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__restrict__ qbar,
                                                               const T *__restrict__ K,
                                                               float *__restrict__ scores,
                                                               Geometry g, int nseg) {
+    constexpr int NQ = D / 16;                   // 16-element chunks of a pooled query
     const int s = blockIdx.y % nseg;             // segment of the query tiles
     const int bg = blockIdx.y / nseg;            // b * Hkv + kv head
     const int hist = s * g.S;                    // history length of the segment's tiles
@@ -86,6 +119,7 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
     const int npairs = ntiles * g.G;             // pair p -> (query head kvh*G + p / ntiles, tile)
     const int j = j0 + (int)threadIdx.x;
     const bool live = j < hist;
+    const int col = threadIdx.x & 15;            // this lane's element of each 16-chunk
 
     float kr[D];
     {
@@ -114,36 +148,71 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
         }
     }
 
-    // pooled queries are wave-uniform: read them through the scalar cache so the
-    // fma chains take them as SGPR operands
-    for (int p0 = 0; p0 < npairs; p0 += SCORE_ILP) {
-        const float *qp[SCORE_ILP];
+    auto unit_of = [&](int pp, int &hq, int &t) -> const float * {
+        hq = pp / ntiles;
+        t = t_first + pp - hq * ntiles;
+        return g.per_seg ? qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.nseg + s) * D
+                         : qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.T + t) * D;
+    };
+    // q[i][c] = pooled query of pair p0 + i, element 16c + col (every row alike),
+    // read as NQ contiguous floats of the lane-major layout
+    auto load_group = [&](float (&q)[SCORE_ILP][NQ], int p0) {
 #pragma unroll
         for (int i = 0; i < SCORE_ILP; ++i) {
-            const int pp = min(p0 + i, npairs - 1);
-            const int hq = pp / ntiles;
-            const int t = t_first + pp - hq * ntiles;
-            qp[i] = g.per_seg ? qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.nseg + s) * D
-                              : qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.T + t) * D;
+            int hq, t;
+            const float *src = unit_of(min(p0 + i, npairs - 1), hq, t) + col * NQ;
+#pragma unroll
+            for (int c = 0; c < NQ; c += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(src + c);
+                q[i][c] = v.x;
+                q[i][c + 1] = v.y;
+                q[i][c + 2] = v.z;
+                q[i][c + 3] = v.w;
+            }
         }
-        float acc[SCORE_ILP];
-#pragma unroll
-        for (int i = 0; i < SCORE_ILP; ++i) acc[i] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < D; ++k) {
-#pragma unroll
-            for (int i = 0; i < SCORE_ILP; ++i) acc[i] = __builtin_fmaf(qp[i][k], kr[k], acc[i]);
-        }
+    };
+    auto store_group = [&](const float (&acc)[SCORE_ILP], int p0) {
 #pragma unroll
         for (int i = 0; i < SCORE_ILP; ++i) {
-            const int pp = p0 + i;
-            if (live && pp < npairs) {
-                const int hq = pp / ntiles;
-                const int t = t_first + pp - hq * ntiles;
+            if (live && p0 + i < npairs) {
+                int hq, t;
+                unit_of(p0 + i, hq, t);
                 scores[list_offset(g, b, kvh * g.G + hq, t) + j] = acc[i];
             }
         }
+    };
+    // Runs the four chains of pairs p0..p0+3 on q.  The previous group's scores
+    // and the next group's loads go out after the first 16 steps, so that when
+    // the next group starts, every memory operation it waits for (loads and
+    // stores share one counter) was issued a whole group earlier.
+    auto run_group = [&](const float (&q)[SCORE_ILP][NQ], int p0, float (&qnext)[SCORE_ILP][NQ],
+                         float (&acc)[SCORE_ILP]) {
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        fma16x4(a0, a1, a2, a3, q[0][0], q[1][0], q[2][0], q[3][0], kr);
+        if (p0 > 0) store_group(acc, p0 - SCORE_ILP);
+        if (p0 + SCORE_ILP < npairs) load_group(qnext, p0 + SCORE_ILP);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 1; c < NQ; ++c)
+            fma16x4(a0, a1, a2, a3, q[0][c], q[1][c], q[2][c], q[3][c], kr + 16 * c);
+        acc[0] = a0;
+        acc[1] = a1;
+        acc[2] = a2;
+        acc[3] = a3;
+    };
+
+    float qa[SCORE_ILP][NQ], qb[SCORE_ILP][NQ], acc[SCORE_ILP];
+    load_group(qa, 0);
+    int p0 = 0;
+    for (;;) {
+        run_group(qa, p0, qb, acc);
+        if (p0 + SCORE_ILP >= npairs) break;
+        p0 += SCORE_ILP;
+        run_group(qb, p0, qa, acc);
+        if (p0 + SCORE_ILP >= npairs) break;
+        p0 += SCORE_ILP;
     }
+    store_group(acc, p0);
 }
 
 }  // namespace

@@ -30,6 +30,8 @@
 //     sharing one KV head are placed on the same XCD so they share its L2.
 #include "s2o_internal.h"
 
+#include <type_traits>
+
 namespace s2o {
 namespace {
 
@@ -635,26 +637,45 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     float m = -INFINITY, l = 0.f;
     const float c = a.scale_log2;
 
-    // per-lane LDS byte offsets of the operand reads
-    const int ka_off = li * C::ROWB, kb_off = (32 + li) * C::ROWB;
+    // Per-lane LDS byte offsets of the operand reads.  With the stage a
+    // compile-time constant (the loop below is unrolled by two), every read is
+    // one of these bases plus an immediate offset, so no VALU computes addresses.
+    //   K (A operand of S^T): step st reads 16-byte piece 2*st + half of rows li
+    //   and 32 + li; both rows share the swizzle (kswz only looks at r & 15 or
+    //   bits 1..3), so the second read is the first plus 32 rows.
+    //   V (A operand of O^T, ds_read_b64_tr_b16): for step s and column block cb
+    //   the lane reads key 16s + 4 v_h + v_e at column 32cb + 16 v_cg + 4 v_rq,
+    //   and the same column of the key 8 further on; the swizzle depends on the
+    //   key only through bits 0..1, which s and the +8 leave alone.
+    constexpr int STEPS = D / 16;
+    int koff[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) koff[st] = li * C::ROWB + (((2 * st + half) ^ kswz<D>(li)) << 4);
     const int gi = lane >> 4, i16 = lane & 15;
     const int v_h = gi >> 1, v_cg = gi & 1, v_e = i16 >> 2, v_rq = i16 & 3;
+    int voff[NACC];
+#pragma unroll
+    for (int cb = 0; cb < NACC; ++cb) {
+        const int key1 = 4 * v_h + v_e, col = 32 * cb + 16 * v_cg + 4 * v_rq;
+        voff[cb] = key1 * C::ROWB + (((col >> 3) ^ vswz<D>(key1)) << 4) + (col & 7) * 2;
+    }
 
-    auto qk = [&](int stage, f32x16 &s0, f32x16 &s1, f32x16 &p0, f32x16 &p1, float m_new, bool exps) {
+    // S^T of the K tile in `stage` (s0: keys 0..31, s1: keys 32..63), with the
+    // exponentials of the previous chunk's probabilities p0/p1 interleaved
+    auto qk = [&](auto stage_c, f32x16 &s0, f32x16 &s1, f32x16 &p0, f32x16 &p1, float m_new, bool exps) {
+        constexpr int stage = decltype(stage_c)::value;
         const unsigned char *Kt = lds + stage * C::TILEB;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-        constexpr int STEPS = D / 16;
         constexpr int EPS = 16 / STEPS;
         bf16x8 ka[2], kb[2];
-        ka[0] = *reinterpret_cast<const bf16x8 *>(Kt + ka_off + ((half ^ kswz<D>(li)) << 4));
-        kb[0] = *reinterpret_cast<const bf16x8 *>(Kt + kb_off + ((half ^ kswz<D>(32 + li)) << 4));
+        ka[0] = *reinterpret_cast<const bf16x8 *>(Kt + koff[0]);
+        kb[0] = *reinterpret_cast<const bf16x8 *>(Kt + koff[0] + 32 * C::ROWB);
 #pragma unroll
         for (int st = 0; st < STEPS; ++st) {
             if (st + 1 < STEPS) {
-                const int pc = 2 * (st + 1) + half;
-                ka[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kt + ka_off + ((pc ^ kswz<D>(li)) << 4));
-                kb[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kt + kb_off + ((pc ^ kswz<D>(32 + li)) << 4));
+                ka[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kt + koff[st + 1]);
+                kb[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kt + koff[st + 1] + 32 * C::ROWB);
             }
             s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1], qf[st], s0, 0, 0, 0);
             s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[st & 1], qf[st], s1, 0, 0, 0);
@@ -682,13 +703,15 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     if (total > 1) fetch_rows(1, vrows);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x16 s0, s1, dummy0, dummy1;
-    qk(0, s0, s1, dummy0, dummy1, 0.f, false);
+    f32x16 sa0, sa1, sb0, sb1;
+    qk(std::integral_constant<int, 0>{}, sa0, sa1, sb0, sb1, 0.f, false);
     __syncthreads();  // every wave has read K stage 0 before it is refilled
 
+    // One chunk k whose K/V sit in stage kst; s holds S_k, sn receives S_{k+1}.
+    // Returns false when the tile stops (or the schedule ends) after chunk k.
     int executed2 = 0;
-    for (int k = 0; k < total; ++k) {
-        const int kst = k & 1;
+    auto iteration = [&](auto kst_c, int k, f32x16 &s0, f32x16 &s1, f32x16 &sn0, f32x16 &sn1) -> bool {
+        constexpr int kst = decltype(kst_c)::value;
         if (k + 2 < total) issue_k(kst, krows);            // K_{k+2} -> stage of K_k
         if (k + 1 < total) issue_v(kst ^ 1, vrows);        // V_{k+1} -> stage of V_{k-1}
         if (k + 3 < total) fetch_rows(k + 3, krows);
@@ -704,8 +727,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
 
         // phase 1: S_{k+1} on the matrix cores with the exponentials of chunk k
         // (stale stage when k+1 == total; the result is unused then)
-        f32x16 sn0, sn1;
-        qk(kst ^ 1, sn0, sn1, s0, s1, m_new, true);
+        qk(std::integral_constant<int, kst ^ 1>{}, sn0, sn1, s0, s1, m_new, true);
         rescale(acc, alpha);
 
         // phase 2: O^T += V^T P^T for chunk k with the row sum
@@ -722,17 +744,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
             }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int key1 = 16 * s + 4 * v_h + v_e;
 #pragma unroll
                 for (int cb = 0; cb < NACC; ++cb) {
-                    const int col = 32 * cb + 16 * v_cg + 4 * v_rq;
-                    const int within = (col & 7) * 2;
-                    const int a1 = key1 * C::ROWB + ((((col >> 3) ^ vswz<D>(key1))) << 4) + within;
-                    const int a2 = (key1 + 8) * C::ROWB + ((((col >> 3) ^ vswz<D>(key1 + 8))) << 4) + within;
+                    const unsigned char *va1 = Vt + voff[cb] + 16 * s * C::ROWB;
                     v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4i16 *)(Vt + a1));
+                        (__attribute__((address_space(3))) v4i16 *)(va1));
                     v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) v4i16 *)(Vt + a2));
+                        (__attribute__((address_space(3))) v4i16 *)(va1 + 8 * C::ROWB));
                     bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
                 }
@@ -753,10 +771,13 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
             int any = 0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) any |= flags[kst][w];
-            if (!any) break;
+            if (!any) return false;
         }
-        s0 = sn0;
-        s1 = sn1;
+        return k + 1 < total;
+    };
+    for (int k = 0;; k += 2) {
+        if (!iteration(std::integral_constant<int, 0>{}, k, sa0, sa1, sb0, sb1)) break;
+        if (!iteration(std::integral_constant<int, 1>{}, k + 1, sb0, sb1, sa0, sa1)) break;
     }
 
     const float inv = 1.0f / l;

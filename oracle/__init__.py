@@ -9,6 +9,10 @@ attention); this module only marshals numpy arrays through ctypes.
 Parity status of each function (the pins live in ``tests/test_oracle_pins.py``):
 
 * ``pool`` / ``score_tile``: pinned (exact special cases, fp64 error bound).
+* ``pool_block`` and block lists: pinned (exact dyadic block means; block
+  scores of block-constant keys equal the key scores, and their block order
+  expands to the key order; tau = 0 equals dense attention; the Q = 0 closed
+  form).
 * ``order``: pinned (permutation, order, ties, independent Python sort).
 * ``attn_tile`` / ``attn_tiles``: pinned (tau = 0 equals dense attention from
   torch's fp64 SDPA; Q = 0 closed form of the stop rule including the equality
@@ -46,7 +50,7 @@ class Problem(ctypes.Structure):
                 ("N", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("seg_len", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("scale", ctypes.c_double),
-                ("per_segment", ctypes.c_int32)]
+                ("per_segment", ctypes.c_int32), ("block_lists", ctypes.c_int32)]
 
 
 _lib = None
@@ -66,6 +70,8 @@ def _load():
             "oracle_pass1_tiles": (i32, [P, ctypes.c_int]),
             "oracle_list_offset": (i64, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
             "oracle_list_entries": (i64, [P]),
+            "oracle_list_len": (i64, [P, ctypes.c_int]),
+            "oracle_pool_block": (None, [P, vp, ctypes.c_int, ctypes.c_int, i64, vp]),
             "oracle_pool": (None, [P, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
             "oracle_rep_query": (None, [P, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
             "oracle_score_tile": (None, [P, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
@@ -88,17 +94,19 @@ def _load():
     return _lib
 
 
-def problem(B, Hq, Hkv, N, d, dtype, seg_len, tile_m, tile_n, scale, per_segment=False) -> Problem:
+def problem(B, Hq, Hkv, N, d, dtype, seg_len, tile_m, tile_n, scale, per_segment=False,
+            block_lists=False) -> Problem:
     """dtype: "f32" (float32 arrays) or "bf16" (uint16 bit-pattern arrays).
-    per_segment: one list per segment (shared by its tiles) instead of per tile."""
+    per_segment: one list per segment (shared by its tiles) instead of per tile.
+    block_lists: list entries are blocks of tile_n keys instead of keys."""
     return Problem(B, Hq, Hkv, N, d, 0 if dtype == "f32" else 1, seg_len, tile_m, tile_n,
-                   float(scale), 1 if per_segment else 0)
+                   float(scale), 1 if per_segment else 0, 1 if block_lists else 0)
 
 
-def problem_from_workload(w, seg_len=None, per_segment=False) -> Problem:
+def problem_from_workload(w, seg_len=None, per_segment=False, block_lists=False) -> Problem:
     return problem(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype,
                    w.seg_len if seg_len is None else seg_len, w.tile_m, w.tile_n, w.scale,
-                   per_segment)
+                   per_segment, block_lists)
 
 
 def _ptr(a):
@@ -132,6 +140,18 @@ def list_entries(p):
     return _load().oracle_list_entries(ctypes.byref(p))
 
 
+def list_len(p, t):
+    """Entries of the list tile t uses (keys, or blocks of tile_n keys)."""
+    return _load().oracle_list_len(ctypes.byref(p), t)
+
+
+def pool_block(p, K, b, g, c):
+    """Mean key of block c of KV head g."""
+    out = np.empty(p.d, dtype=np.float32)
+    _load().oracle_pool_block(ctypes.byref(p), _ptr(_check(K, p, "K")), b, g, c, _ptr(out))
+    return out
+
+
 def num_threads():
     return _load().oracle_num_threads()
 
@@ -150,7 +170,7 @@ def rep_query(p, Q, b, h, t):
 
 
 def score_tile(p, Q, K, b, h, t):
-    a = seg_start(p, t)
+    a = list_len(p, t)
     out = np.empty(max(a, 1), dtype=np.float32)
     _load().oracle_score_tile(ctypes.byref(p), _ptr(_check(Q, p, "Q")), _ptr(_check(K, p, "K")),
                               b, h, t, _ptr(out))
@@ -167,13 +187,13 @@ def order(scores):
 def attn_tile(p, Q, K, V, b, h, t, lst, tau, force_n=0):
     """Returns (out [BM, d] float64, n_exec, chunks executed, gstar per chunk)."""
     lib = _load()
-    a = seg_start(p, t)
+    a = list_len(p, t)
     lst = np.ascontiguousarray(lst, dtype=np.int32)
     if len(lst) != a:
-        raise ValueError("list length must equal the tile's history length")
+        raise ValueError("list length must equal the tile's list length")
     out = np.empty((p.tile_m, p.d), dtype=np.float64)
     n_exec = ctypes.c_int32()
-    gstar = np.zeros(max(a // p.tile_n, 1), dtype=np.float64)
+    gstar = np.zeros(max(seg_start(p, t) // p.tile_n, 1), dtype=np.float64)
     buf = lst if a > 0 else np.zeros(1, dtype=np.int32)
     c = lib.oracle_attn_tile(ctypes.byref(p), _ptr(_check(Q, p, "Q")), _ptr(_check(K, p, "K")),
                              _ptr(_check(V, p, "V")), b, h, t, _ptr(buf), float(tau),
@@ -191,8 +211,8 @@ def attn_tiles(p, Q, K, V, tiles, tau, lists=None, force_n=None, want_lists=Fals
     lib = _load()
     tiles = np.ascontiguousarray(np.asarray(tiles, dtype=np.int32).reshape(-1, 3))
     n = len(tiles)
-    max_list = max([seg_start(p, int(t)) for _, _, t in tiles] + [1])
-    max_chunks = max(max_list // p.tile_n, 1)
+    max_list = max([list_len(p, int(t)) for _, _, t in tiles] + [1])
+    max_chunks = max(max([seg_start(p, int(t)) for _, _, t in tiles] + [1]) // p.tile_n, 1)
     out = np.empty((n, p.tile_m, p.d), dtype=np.float64)
     n_exec = np.empty(n, dtype=np.int32)
     chunks = np.empty(n, dtype=np.int32)

@@ -36,8 +36,17 @@
  *              representative query of the segment): the mean of the
  *              segment's tile queries, an fp32 sum over its tiles in
  *              ascending order times fl(1/number of tiles).
- *   order      the list: history keys sorted by score descending, ties to the
- *              lower index ([GIST] KV_perm: indices form a global logical map).
+ *   block lists (optional granularity): entries are blocks of BN consecutive
+ *              history keys instead of single keys.  Block c is scored with
+ *              its mean key (fp32 sum of its BN rows in ascending order, then
+ *              the exact power-of-two scaling), with the same fma chain; pass
+ *              2 chunk c is then the BN keys of the c-th listed block.  This is
+ *              the block-granularity counterpart the pages compare against
+ *              ([ABS] and [GIST] contrast token-level ordering with block-level
+ *              sparse attention).
+ *   order      the list: history keys (or blocks) sorted by score descending,
+ *              ties to the lower index ([GIST] KV_perm: indices form a global
+ *              logical map).
  *   pass 1     for each row i, online softmax over keys [a_t, i] in BN-wide key
  *              tiles in ascending order ([GIST] Passage 1: dense causal window
  *              inside the current segment, initialising (m, l, acc)).
@@ -74,6 +83,7 @@ typedef struct {
     int32_t seg_len, tile_m, tile_n;
     double scale;
     int32_t per_segment; /* 0: one list per query tile; 1: one list per segment */
+    int32_t block_lists; /* 0: entries are keys; 1: entries are blocks of tile_n keys */
 } oracle_problem;
 
 /* ---- element access ------------------------------------------------------ */
@@ -116,12 +126,18 @@ int32_t oracle_pass1_tiles(const oracle_problem *p, int t) {
  * are empty. */
 static int32_t num_segments(const oracle_problem *p) { return (p->N + p->seg_len - 1) / p->seg_len; }
 
+/* keys covered by one list entry */
+static int64_t entry_keys(const oracle_problem *p) { return p->block_lists ? p->tile_n : 1; }
+
+/* entries of the list tile t uses: its history length in keys or in blocks */
+int64_t oracle_list_len(const oracle_problem *p, int t) { return oracle_seg_start(p, t) / entry_keys(p); }
+
 static int64_t per_head_entries(const oracle_problem *p) {
     int64_t total = 0;
     if (p->per_segment) {
-        for (int s = 0; s < num_segments(p); ++s) total += (int64_t)s * p->seg_len;
+        for (int s = 0; s < num_segments(p); ++s) total += (int64_t)s * p->seg_len / entry_keys(p);
     } else {
-        for (int u = 0; u < oracle_num_tiles(p); ++u) total += oracle_seg_start(p, u);
+        for (int u = 0; u < oracle_num_tiles(p); ++u) total += oracle_list_len(p, u);
     }
     return total;
 }
@@ -130,9 +146,9 @@ int64_t oracle_list_offset(const oracle_problem *p, int b, int h, int t) {
     int64_t off = ((int64_t)b * p->Hq + h) * per_head_entries(p);
     if (p->per_segment) {
         int seg = (int)(oracle_seg_start(p, t) / p->seg_len);
-        for (int s = 0; s < seg; ++s) off += (int64_t)s * p->seg_len;
+        for (int s = 0; s < seg; ++s) off += (int64_t)s * p->seg_len / entry_keys(p);
     } else {
-        for (int u = 0; u < t; ++u) off += oracle_seg_start(p, u);
+        for (int u = 0; u < t; ++u) off += oracle_list_len(p, u);
     }
     return off;
 }
@@ -179,19 +195,38 @@ void oracle_rep_query(const oracle_problem *p, const void *Q, int b, int h, int 
     free(tq);
 }
 
-/* Scores of the history keys of the list tile t uses: s[j] = fmaf chain over
- * k = 0..d-1. */
+/* Mean key of block c (keys c*BN .. c*BN+BN-1) of KV head g: fp32 sum of the
+ * BN rows in ascending order, then the exact power-of-two scaling (BN must be
+ * a power of two). */
+void oracle_pool_block(const oracle_problem *p, const void *K, int b, int g, int64_t c, float *kbar) {
+    float inv = 1.0f / (float)p->tile_n;
+    for (int k = 0; k < p->d; ++k) {
+        float sum = 0.0f;
+        for (int r = 0; r < p->tile_n; ++r)
+            sum = sum + widen(K, p->dtype, kv_index(p, b, g, c * p->tile_n + r, k));
+        kbar[k] = sum * inv;
+    }
+}
+
+/* Scores of the entries of the list tile t uses: s[j] = fmaf chain over
+ * k = 0..d-1 of qbar[k] times key j (or the mean key of block j). */
 void oracle_score_tile(const oracle_problem *p, const void *Q, const void *K, int b, int h,
                        int t, float *scores) {
     int g = h / (p->Hq / p->Hkv);
-    int64_t a = oracle_seg_start(p, t);
+    int64_t n = oracle_list_len(p, t);
     float *qbar = (float *)malloc(sizeof(float) * p->d);
+    float *kbar = (float *)malloc(sizeof(float) * p->d);
     oracle_rep_query(p, Q, b, h, t, qbar);
-    for (int64_t j = 0; j < a; ++j) {
+    for (int64_t j = 0; j < n; ++j) {
+        if (p->block_lists)
+            oracle_pool_block(p, K, b, g, j, kbar);
+        else
+            for (int k = 0; k < p->d; ++k) kbar[k] = widen(K, p->dtype, kv_index(p, b, g, j, k));
         float acc = 0.0f;
-        for (int k = 0; k < p->d; ++k) acc = fmaf(qbar[k], widen(K, p->dtype, kv_index(p, b, g, j, k)), acc);
+        for (int k = 0; k < p->d; ++k) acc = fmaf(qbar[k], kbar[k], acc);
         scores[j] = acc;
     }
+    free(kbar);
     free(qbar);
 }
 
@@ -263,7 +298,7 @@ static double absorb(const oracle_problem *p, const void *Q, const void *K, cons
 
 /*
  * One query tile.  `list` holds the tile's a_t history indices in visiting
- * order.  tau >= 0.  force_n > 0 executes exactly min(force_n, C_t) pass-2
+ * order (block lists: its a_t / BN block indices; chunk c is block list[c]).  tau >= 0.  force_n > 0 executes exactly min(force_n, C_t) pass-2
  * chunks regardless of tau (used to re-check a tile at a given chunk count).
  * Outputs: out[BM*d] in double, *n_exec = pass-1 tiles + executed chunks,
  * gstar[c] = max_i g_i of chunk c for the executed chunks (may be NULL).
@@ -304,7 +339,8 @@ int32_t oracle_attn_tile(const oracle_problem *p, const void *Q, const void *K, 
     int32_t executed = 0;
     int32_t limit = (force_n > 0 && force_n < chunks) ? force_n : chunks;
     for (int32_t c = 0; c < limit; ++c) {
-        for (int e = 0; e < BN; ++e) keys[e] = list[(int64_t)c * BN + e];
+        for (int e = 0; e < BN; ++e)
+            keys[e] = p->block_lists ? (int64_t)list[c] * BN + e : list[(int64_t)c * BN + e];
         double worst = 0.0; /* max over rows of g_i */
         for (int r = 0; r < BM; ++r) {
             double mass = absorb(p, Q, K, V, b, h, g, row0 + r, keys, BN, &st[r], x);
@@ -377,7 +413,7 @@ void oracle_scores_all(const oracle_problem *p, const void *Q, const void *K, fl
     for (int64_t u = 0; u < units; ++u) {
         int b = (int)(u / ((int64_t)p->Hq * U)), h = (int)((u / U) % p->Hq);
         int t = list_owner(p, (int)(u % U));
-        if (oracle_seg_start(p, t) > 0)
+        if (oracle_list_len(p, t) > 0)
             oracle_score_tile(p, Q, K, b, h, t, scores + oracle_list_offset(p, b, h, t));
     }
 }
@@ -391,7 +427,7 @@ void oracle_lists_all(const oracle_problem *p, const float *scores, int32_t *lis
         int b = (int)(u / ((int64_t)p->Hq * U)), h = (int)((u / U) % p->Hq);
         int t = list_owner(p, (int)(u % U));
         int64_t off = oracle_list_offset(p, b, h, t);
-        oracle_order(scores + off, oracle_seg_start(p, t), lists + off);
+        oracle_order(scores + off, oracle_list_len(p, t), lists + off);
     }
 }
 
@@ -412,7 +448,7 @@ void oracle_attn_tiles(const oracle_problem *p, const void *Q, const void *K, co
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t n = 0; n < n_tiles; ++n) {
         int b = tiles[3 * n], h = tiles[3 * n + 1], t = tiles[3 * n + 2];
-        int64_t a = oracle_seg_start(p, t);
+        int64_t a = oracle_list_len(p, t);
         int32_t *list;
         int32_t *owned = NULL;
         if (lists_in) {

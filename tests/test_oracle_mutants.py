@@ -21,8 +21,8 @@ MUTANTS = {
     "pool drops the last row": ("for (int r = 0; r < p->tile_m; ++r)",
                                 "for (int r = 0; r < p->tile_m - 1; ++r)"),
     "score reads the wrong KV head": (
-        "int g = h / (p->Hq / p->Hkv);\n    int64_t a = oracle_seg_start(p, t);\n    float *qbar",
-        "int g = h % p->Hkv;\n    int64_t a = oracle_seg_start(p, t);\n    float *qbar"),
+        "int g = h / (p->Hq / p->Hkv);\n    int64_t n = oracle_list_len(p, t);",
+        "int g = h % p->Hkv;\n    int64_t n = oracle_list_len(p, t);"),
     "ties go to the higher index": ("return (a->j > c->j) - (a->j < c->j);",
                                     "return (a->j < c->j) - (a->j > c->j);"),
     "list sorted ascending": ("if (a->s > c->s) return -1;\n    if (a->s < c->s) return 1;",
@@ -47,6 +47,11 @@ MUTANTS = {
     "pass 2 skips its first chunk": ("for (int32_t c = 0; c < limit; ++c) {", "for (int32_t c = 1; c < limit; ++c) {"),
     "segment mean drops its last tile": ("for (int u = first; u < last; ++u) {", "for (int u = first; u < last - 1; ++u) {"),
     "segment lists keyed by tile": ("int seg = (int)(oracle_seg_start(p, t) / p->seg_len);", "int seg = t % num_segments(p);"),
+    "block mean drops a row": ("for (int r = 0; r < p->tile_n; ++r)", "for (int r = 1; r < p->tile_n; ++r)"),
+    "block chunk ignores the list": ("keys[e] = p->block_lists ? (int64_t)list[c] * BN + e",
+                                     "keys[e] = p->block_lists ? (int64_t)c * BN + e"),
+    "block scored by its first key": ("            oracle_pool_block(p, K, b, g, j, kbar);",
+                                      "            for (int k = 0; k < p->d; ++k) kbar[k] = widen(K, p->dtype, kv_index(p, b, g, j * p->tile_n, k));"),
 }
 
 

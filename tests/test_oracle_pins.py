@@ -518,3 +518,114 @@ def test_segment_representative_exact_on_dyadic_inputs():
         want = [Fraction(int(x)) for x in vals[first:first + S // BM].astype(np.int64).sum(axis=0)]
         want = [w / (S // BM) for w in want]
         assert [Fraction(float(x)) for x in oracle.rep_query(p, Q, 0, 0, t)] == want
+
+
+# ------------------------------------------------------------- block lists ---
+# List entries are blocks of BN consecutive keys, scored with the block's mean
+# key; pass-2 chunk c is the c-th listed block.  The pages contrast S2O's
+# token-level ordering with block-level sparse attention (authors' abstract;
+# gist.science summary, "Signification et Revendications"), so the block form is
+# the counterpart used for that comparison.
+
+@pytest.mark.parametrize("geom", GEOMS)
+def test_block_lists_tau_zero_equals_dense_attention(geom):
+    B, Hq, Hkv, N, d, S, BM, BN, dt = geom
+    Q, K, V = random_inputs(B, Hq, Hkv, N, d, seed=131 + N, dtype=dt)
+    for per_segment in (False, True):
+        p = oracle.problem(B, Hq, Hkv, N, d, dt, S, BM, BN, 1 / np.sqrt(d), per_segment=per_segment,
+                           block_lists=True)
+        out, _, _, _ = run_all(p, Q, K, V, 0.0)
+        np.testing.assert_allclose(out, sdpa_fp64(p, Q, K, V), rtol=0, atol=1e-12)
+
+
+def test_block_list_layout():
+    """A block list has a_t / BN entries; offsets walk (b, h, t) over those lengths."""
+    S, BM, BN, N = 48, 8, 4, 200
+    p = oracle.problem(2, 4, 2, N, 16, "f32", S, BM, BN, 0.25, block_lists=True)
+    T = N // BM
+    lens = [(t * BM // S) * S // BN for t in range(T)]
+    assert oracle.list_entries(p) == 2 * 4 * sum(lens)
+    for b, h, t in [(0, 0, 0), (0, 3, 7), (1, 2, 24), (1, 3, T - 1)]:
+        assert oracle.list_len(p, t) == lens[t]
+        assert oracle.list_offset(p, b, h, t) == (b * 4 + h) * sum(lens) + sum(lens[:t])
+
+
+def test_block_mean_exact_on_dyadic_inputs():
+    """Small integer keys: every fp32 partial sum is exact and BN is a power of two, so the
+    block mean is the exact mean."""
+    N, d, BN = 256, 8, 16
+    rng = np.random.default_rng(4)
+    K = rng.integers(-40, 41, size=(1, 2, N, d)).astype(np.float32)
+    p = oracle.problem(1, 2, 2, N, d, "f32", 64, 16, BN, 1.0, block_lists=True)
+    for g in range(2):
+        for c in (0, 3, N // BN - 1):
+            want = [Fraction(int(x), BN) for x in K[0, g, c * BN:(c + 1) * BN].astype(np.int64).sum(axis=0)]
+            assert [Fraction(float(x)) for x in oracle.pool_block(p, K, 0, g, c)] == want
+
+
+def test_block_scores_of_block_constant_keys_match_key_scores():
+    """Keys constant within each block: the block mean is that key exactly, so each block
+    score equals the score of any of its keys, and the block order expanded to keys is the
+    key order (ties inside a block go to the lower index in both)."""
+    B, Hq, Hkv, N, d, S, BM, BN = 1, 2, 1, 512, 16, 128, 32, 16
+    rng = np.random.default_rng(6)
+    Kb = (rng.integers(-20, 21, size=(N // BN, d)) / 8).astype(np.float32)  # block sums exact
+    K = np.repeat(Kb, BN, axis=0).reshape(1, 1, N, d)
+    Q = rng.standard_normal((1, Hq, N, d)).astype(np.float32)
+    V = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    pk = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, BN, 0.25)
+    pb = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, BN, 0.25, block_lists=True)
+    for h in range(Hq):
+        for t in (4, 9, 15):
+            sk = oracle.score_tile(pk, Q, K, 0, h, t)
+            sb = oracle.score_tile(pb, Q, K, 0, h, t)
+            assert np.array_equal(sb, sk[::BN])
+            lk = oracle.order(sk)
+            lb = oracle.order(sb)
+            assert np.array_equal((lb[:, None] * BN + np.arange(BN)).ravel(), lk)
+    ok, nk, _, _ = run_all(pk, Q, K, V, 0.01)
+    ob, nb, _, _ = run_all(pb, Q, K, V, 0.01)
+    assert np.array_equal(ok, ob) and np.array_equal(nk, nb)
+
+
+@pytest.mark.parametrize("BM,BN,S,N,tau", [(16, 8, 64, 256, 0.05), (8, 4, 32, 256, 0.1),
+                                           (16, 16, 32, 256, 1.0)])
+def test_block_lists_q_zero_closed_form(BM, BN, S, N, tau):
+    """Q = 0: every block scores 0, the block list ascends, so the visited keys and the
+    stop follow the same closed form as key lists."""
+    d = 4
+    rng = np.random.default_rng(BM * 100 + BN)
+    Q = np.zeros((1, 1, N, d), dtype=np.float32)
+    K = f32(rng.standard_normal((1, 1, N, d)))
+    V = f32(rng.standard_normal((1, 1, N, d)))
+    p = oracle.problem(1, 1, 1, N, d, "f32", S, BM, BN, 0.5, block_lists=True)
+    out, n_exec, chunks, r = run_all(p, Q, K, V, tau)
+    for t in range(N // BM):
+        a, n = q_zero_prediction(BM, BN, S, t, tau)
+        assert np.array_equal(r["lists"][t, :a // BN], np.arange(a // BN))
+        assert chunks[0, 0, t] == n and n_exec[0, 0, t] == ((t + 1) * BM - a) // BN + n
+        for r_ in (0, BM - 1):
+            i = t * BM + r_
+            keys = list(range(a, i + 1)) + list(range(n * BN))
+            np.testing.assert_allclose(out[0, 0, i], V[0, 0, keys].astype(np.float64).mean(axis=0),
+                                       rtol=0, atol=1e-12)
+
+
+def test_block_scores_exact_on_dyadic_inputs():
+    """Constant integer query rows and small integer keys that vary inside each block:
+    the pooled query, the block means and every fma step are exact, so each block score is
+    the exact dot product of the query with the block's mean key."""
+    N, d, BM, BN, S = 256, 8, 16, 16, 64
+    rng = np.random.default_rng(8)
+    K = rng.integers(-8, 9, size=(1, 1, N, d)).astype(np.float32)
+    qrow = rng.integers(-3, 4, size=d).astype(np.float32)
+    Q = np.tile(qrow, (1, 1, N, 1)).astype(np.float32)
+    p = oracle.problem(1, 1, 1, N, d, "f32", S, BM, BN, 1.0, block_lists=True)
+    for t in (4, 8, 15):
+        a = t * BM // S * S
+        got = oracle.score_tile(p, Q, np.ascontiguousarray(K), 0, 0, t)
+        assert len(got) == a // BN
+        for c in range(a // BN):
+            block = K[0, 0, c * BN:(c + 1) * BN].astype(np.int64)
+            want = sum(Fraction(int(qrow[k])) * Fraction(int(block[:, k].sum()), BN) for k in range(d))
+            assert Fraction(float(got[c])) == want

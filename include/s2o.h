@@ -40,6 +40,8 @@
  *     off(b, h, t) = (b*Hq + h)*L + S*(P*s*(s-1)/2 + (t - s*P)*s).
  *   Per-segment lists: one per (b, h, s), list s has s*S entries,
  *     off(b, h, s) = (b*Hq + h)*L + S*s*(s-1)/2, and tile t uses list floor(t/P).
+ *   Block lists: the same layouts with every length and history term divided
+ *     by tile_n; idx values are block numbers in [0, a_t / tile_n).
  *   Entries are int64-addressed; idx values are key positions in [0, a_t).
  */
 #ifndef S2O_H
@@ -75,16 +77,26 @@ typedef struct {
     int32_t tile_m;   /* BM: 64 or 128 */
     int32_t tile_n;   /* BN: 64 */
     float scale;      /* softmax scale (1/sqrt(d) for standard attention), finite */
-    int32_t list_granularity; /* S2O_LISTS_PER_TILE (0) or S2O_LISTS_PER_SEGMENT (1) */
+    int32_t list_granularity; /* one of the S2O_LISTS_* values below */
 } s2o_problem;
 
-/* Which query a list is ranked against ([GIST] KV_perm):
+/* Which query a list is ranked against ([GIST] KV_perm), and what an entry is.
  *   S2O_LISTS_PER_TILE: one list per (b, h, query tile), ranked against the
  *     tile's mean query;
  *   S2O_LISTS_PER_SEGMENT: one list per (b, h, segment), shared by the
  *     segment's tiles and ranked against the segment's representative query =
- *     fp32 sum of its tile means in ascending tile order times fl(1/tiles). */
-enum { S2O_LISTS_PER_TILE = 0, S2O_LISTS_PER_SEGMENT = 1 };
+ *     fp32 sum of its tile means in ascending tile order times fl(1/tiles).
+ *   ..._BLOCKS: the same lists with blocks of tile_n consecutive keys as
+ *     entries (the block-granularity counterpart the pages compare S2O with,
+ *     [ABS]): block c is scored with its mean key (fp32 sum of its rows in
+ *     ascending order, times 1/tile_n), every list is 1/tile_n as long, and
+ *     pass-2 chunk c is the tile_n keys of the c-th listed block. */
+enum {
+    S2O_LISTS_PER_TILE = 0,
+    S2O_LISTS_PER_SEGMENT = 1,
+    S2O_LISTS_PER_TILE_BLOCKS = 2,
+    S2O_LISTS_PER_SEGMENT_BLOCKS = 3
+};
 
 /* Validates a problem (sizes, divisibility, supported tiles).  Returns S2O_OK,
  * S2O_ERR_INVALID_ARG or S2O_ERR_UNSUPPORTED.  Pure host function. */
@@ -99,8 +111,8 @@ int64_t s2o_list_entries(const s2o_problem *p);
 int64_t s2o_list_offset(const s2o_problem *p, int32_t b, int32_t h, int32_t t);
 
 /* Bytes of device workspace s2o_score needs (the pooled query of every tile
- * and, for per-segment lists, of every segment, fp32).  0 if the problem is
- * invalid. */
+ * and, for per-segment lists, of every segment; for block lists also the mean
+ * key of every block; all fp32).  0 if the problem is invalid. */
 size_t s2o_score_workspace_bytes(const s2o_problem *p);
 
 /* Importance estimator ([GIST] KV_perm: history keys are scored against a

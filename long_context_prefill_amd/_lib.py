@@ -84,18 +84,20 @@ def _raise(fn: str, st: int):
         raise S2OError(fn, st, lib().s2o_status_string(st).decode())
 
 
-LISTS_PER_TILE, LISTS_PER_SEGMENT = 0, 1
+LISTS = {"tile": 0, "segment": 1, "tile_blocks": 2, "segment_blocks": 3}
+LISTS_PER_TILE, LISTS_PER_SEGMENT = LISTS["tile"], LISTS["segment"]
 
 
 def problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, seg_len, tile_m=128,
             tile_n=64, scale=None, causal=True, lists="tile") -> Problem:
     """dtype: torch.float32 / torch.bfloat16 (or 0 / 1).
-    lists: "tile" (one list per query tile) or "segment" (one list per segment)."""
+    lists: "tile" (one list per query tile), "segment" (one list per segment), or
+    "tile_blocks" / "segment_blocks" (the same with blocks of tile_n keys as entries)."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
-    gran = {"tile": LISTS_PER_TILE, "segment": LISTS_PER_SEGMENT}[lists]
+    gran = LISTS[lists]
     return Problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, 1 if causal else 0,
                    seg_len, tile_m, tile_n, float(scale), gran)
 
@@ -156,7 +158,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def s2o_score(p: Problem, q: torch.Tensor, k: torch.Tensor, scores: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """fp32 importance scores of every tile's history keys, in the list layout."""
+    """fp32 importance scores of every list entry (history keys or blocks), in the list layout."""
     dt = _tdtype(p)
     n = list_entries(p)
     if scores is None:
@@ -173,7 +175,7 @@ def s2o_score(p: Problem, q: torch.Tensor, k: torch.Tensor, scores: Optional[tor
 
 def s2o_build_index(p: Problem, scores: torch.Tensor, idx: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Per-tile key lists, score descending, ties to the lower position."""
+    """Index lists (keys or blocks), score descending, ties to the lower position."""
     n = list_entries(p)
     if idx is None:
         idx = torch.empty(n, dtype=torch.int32, device=scores.device)

@@ -30,7 +30,7 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     if (p->head_dim != 64 && p->head_dim != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_m != 64 && p->tile_m != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_n != s2o::kTileN) return S2O_ERR_UNSUPPORTED;
-    if (p->list_granularity != S2O_LISTS_PER_TILE && p->list_granularity != S2O_LISTS_PER_SEGMENT)
+    if (p->list_granularity < S2O_LISTS_PER_TILE || p->list_granularity > S2O_LISTS_PER_SEGMENT_BLOCKS)
         return S2O_ERR_INVALID_ARG;
 
     g.B = p->batch;
@@ -47,7 +47,8 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     g.causal = p->causal;
     g.dtype = p->dtype;
     g.scale = p->scale;
-    g.per_seg = p->list_granularity == S2O_LISTS_PER_SEGMENT;
+    g.per_seg = p->list_granularity & 1;
+    g.blocks = (p->list_granularity >> 1) & 1;
     g.nseg = (g.N + g.S - 1) / g.S;
     g.inv_P = 1.0f / (float)g.P;
     g.inv_P_last = 1.0f / (float)(g.T - (g.nseg - 1) * g.P);
@@ -59,6 +60,7 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
         if (first + tiles > g.T) tiles = g.T - first;
         L += (g.per_seg ? 1 : tiles) * s * g.S;
     }
+    if (g.blocks) L /= g.BN;  // every history is a multiple of S, and S of BN
     g.list_per_head = L;
     g.list_entries = L * g.B * g.Hq;
     // index ranges the kernels assume
@@ -67,9 +69,11 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
         return S2O_ERR_UNSUPPORTED;
     const int64_t nseg = (g.N + g.S - 1) / g.S;
     if ((int64_t)g.B * g.Hkv * nseg > 65535) return S2O_ERR_UNSUPPORTED;
-    int64_t e = g.S & (-g.S);
+    const Geometry lg = g.blocks ? s2o::block_geometry(g) : g;
+    int64_t e = lg.S & (-lg.S);
     if (e > 4096) e = 4096;
-    if (g.list_entries / e >= (1ll << 31)) return S2O_ERR_UNSUPPORTED;
+    if (lg.list_entries / e >= (1ll << 31)) return S2O_ERR_UNSUPPORTED;
+    if (!s2o::sort_supported(lg)) return S2O_ERR_UNSUPPORTED;
     return S2O_OK;
 }
 
@@ -104,14 +108,18 @@ int64_t s2o_list_offset(const s2o_problem *p, int32_t b, int32_t h, int32_t t) {
 }
 
 namespace {
+Geometry list_geometry(const Geometry &g) { return g.blocks ? s2o::block_geometry(g) : g; }
 size_t tile_query_bytes(const Geometry &g) { return ((size_t)g.B * g.Hq * g.T * g.d * sizeof(float) + 255) & ~(size_t)255; }
+size_t segment_query_bytes(const Geometry &g) {
+    return g.per_seg ? (((size_t)g.B * g.Hq * g.nseg * g.d * sizeof(float) + 255) & ~(size_t)255) : 0;
+}
 }
 
 size_t s2o_score_workspace_bytes(const s2o_problem *p) {
     Geometry g;
     if (make_geometry(p, g) != S2O_OK) return 0;
-    size_t seg = g.per_seg ? (size_t)g.B * g.Hq * g.nseg * g.d * sizeof(float) : 0;
-    return tile_query_bytes(g) + seg;
+    const size_t blocks = g.blocks ? (size_t)g.B * g.Hkv * (g.N / g.BN) * g.d * sizeof(float) : 0;
+    return tile_query_bytes(g) + segment_query_bytes(g) + blocks;
 }
 
 s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *scores,
@@ -125,18 +133,23 @@ s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *
     if (!workspace_ok(workspace, workspace_bytes, s2o_score_workspace_bytes(p))) return S2O_ERR_WORKSPACE;
     if (g.list_entries == 0) return S2O_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    float *qbar = reinterpret_cast<float *>(workspace);
-    float *qseg = g.per_seg ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + tile_query_bytes(g))
-                            : nullptr;
+    char *ws = reinterpret_cast<char *>(workspace);
+    float *qbar = reinterpret_cast<float *>(ws);
+    float *qseg = g.per_seg ? reinterpret_cast<float *>(ws + tile_query_bytes(g)) : nullptr;
     hipError_t e = s2o::launch_pool(g, Q, qbar, qseg, s);
     if (e != hipSuccess) return S2O_ERR_HIP;
-    return launch_status(s2o::launch_score(g, g.per_seg ? qseg : qbar, K, scores, s));
+    if (!g.blocks) return launch_status(s2o::launch_score(g, g.per_seg ? qseg : qbar, K, scores, s));
+    // block lists: score the blocks' mean keys as the keys of the block geometry
+    float *kbar = reinterpret_cast<float *>(ws + tile_query_bytes(g) + segment_query_bytes(g));
+    e = s2o::launch_pool_blocks(g, K, kbar, s);
+    if (e != hipSuccess) return S2O_ERR_HIP;
+    return launch_status(s2o::launch_score(s2o::block_geometry(g), g.per_seg ? qseg : qbar, kbar, scores, s));
 }
 
 size_t s2o_build_index_workspace_bytes(const s2o_problem *p) {
     Geometry g;
     if (make_geometry(p, g) != S2O_OK) return 0;
-    return s2o::sort_workspace_bytes(g);
+    return s2o::sort_workspace_bytes(list_geometry(g));
 }
 
 s2o_status s2o_build_index(const s2o_problem *p, const float *scores, int32_t *idx,
@@ -147,9 +160,10 @@ s2o_status s2o_build_index(const s2o_problem *p, const float *scores, int32_t *i
     if (!g.causal) return S2O_ERR_UNSUPPORTED;
     if (g.list_entries > 0 && (!scores || !idx || !aligned16(scores) || !aligned16(idx)))
         return S2O_ERR_INVALID_ARG;
-    if (!workspace_ok(workspace, workspace_bytes, s2o::sort_workspace_bytes(g))) return S2O_ERR_WORKSPACE;
+    const Geometry lg = list_geometry(g);
+    if (!workspace_ok(workspace, workspace_bytes, s2o::sort_workspace_bytes(lg))) return S2O_ERR_WORKSPACE;
     if (g.list_entries == 0) return S2O_OK;
-    return launch_status(s2o::launch_sort(g, scores, idx, workspace, reinterpret_cast<hipStream_t>(stream)));
+    return launch_status(s2o::launch_sort(lg, scores, idx, workspace, reinterpret_cast<hipStream_t>(stream)));
 }
 
 s2o_status s2o_attn_fwd(const s2o_problem *p, const void *Q, const void *K, const void *V,

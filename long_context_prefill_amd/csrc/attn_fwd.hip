@@ -211,7 +211,8 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
     const T *Vp = reinterpret_cast<const T *>(a.v) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
 
     auto chunk_row = [&](int k, int p) -> int {
-        return k < n1 ? base1 + k * BN + p : list[(k - n1) * BN + p];
+        if (k < n1) return base1 + k * BN + p;
+        return g.blocks ? list[k - n1] * BN + p : list[(k - n1) * BN + p];
     };
 
     // ---- per-thread staging geometry
@@ -591,7 +592,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     const __bf16 *Vp = reinterpret_cast<const __bf16 *>(a.v) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
 
     auto chunk_row = [&](int k, int p) -> int {
-        return k < n1 ? base1 + k * BN + p : list[(k - n1) * BN + p];
+        if (k < n1) return base1 + k * BN + p;
+        return g.blocks ? list[k - n1] * BN + p : list[(k - n1) * BN + p];
     };
     // slot q = (wave*INSTR + i)*64 + lane of a tile: row q / CPR, slot q % CPR
     auto slot_row = [&](int i) { return ((wave * C::INSTR + i) * 64 + lane) / C::CPR; };

@@ -17,6 +17,7 @@ struct Geometry {
     int32_t causal;
     int32_t dtype;           // 0 fp32, 1 bf16
     int32_t per_seg;         // lists per segment (1) or per query tile (0)
+    int32_t blocks;          // list entries are blocks of BN keys (1) or keys (0)
     int32_t nseg;            // segments, the last one possibly partial
     float inv_P, inv_P_last; // fl(1/tiles) of a full and of the last segment
     int64_t list_per_head;   // L: list entries of one (b, h)
@@ -27,10 +28,13 @@ struct Geometry {
 // Offset of the list tile t of (b, h) uses:
 //   per tile:    (b*Hq+h)*L + S*(P*s*(s-1)/2 + (t - s*P)*s), s = t / P
 //   per segment: (b*Hq+h)*L + S*s*(s-1)/2
+// with block entries every list is 1/BN as long (S is a multiple of BN), so the
+// history term is divided by BN.
 __host__ __device__ inline int64_t list_offset(const Geometry &g, int b, int h, int t) {
     int64_t s = t / g.P;
     int64_t within = g.per_seg ? (int64_t)g.S * (s * (s - 1) / 2)
                                : (int64_t)g.S * (g.P * s * (s - 1) / 2 + (t - s * g.P) * s);
+    if (g.blocks) within /= g.BN;
     return ((int64_t)b * g.Hq + h) * g.list_per_head + within;
 }
 
@@ -42,16 +46,32 @@ __host__ __device__ inline int64_t seg_start(const Geometry &g, int t) {
     return ((int64_t)t * g.BM / g.S) * g.S;
 }
 
+// Block lists as a key problem of their own: each block becomes one "key" (its
+// mean row, fp32), so N, S and BM shrink by BN and the lists keep their layout.
+// Scoring and sorting run unchanged on this geometry.
+inline Geometry block_geometry(const Geometry &g) {
+    Geometry b = g;
+    b.N = g.N / g.BN;
+    b.S = g.S / g.BN;
+    b.BM = g.BM / g.BN;
+    b.BN = 1;
+    b.blocks = 0;
+    b.dtype = 0;
+    return b;
+}
+
 // Kernel launchers (return hipSuccess or the launch error).
 hipError_t launch_attention(const Geometry &g, const void *Q, const void *K, const void *V,
                             const int32_t *idx, float tau, void *O, int32_t *exec_tiles,
                             bool s2o, hipStream_t stream);
 
 hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, float *qseg, hipStream_t stream);
+hipError_t launch_pool_blocks(const Geometry &g, const void *K, float *kbar, hipStream_t stream);
 hipError_t launch_score(const Geometry &g, const float *qrep, const void *K, float *scores,
                         hipStream_t stream);
 
 size_t sort_workspace_bytes(const Geometry &g);
+bool sort_supported(const Geometry &g);  // false: lists too long for blocks this small
 hipError_t launch_sort(const Geometry &g, const float *scores, int32_t *idx, void *ws,
                        hipStream_t stream);
 

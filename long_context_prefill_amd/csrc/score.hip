@@ -69,6 +69,22 @@ __global__ __launch_bounds__(256) void segpool_kernel(const float *__restrict__ 
     qseg[gid] = sum * (s == g.nseg - 1 ? g.inv_P_last : g.inv_P);
 }
 
+// Block lists: the mean key of every block of BN keys, fp32 sum of its rows in
+// ascending order times 1/BN (exact: BN is a power of two), stored
+// [B, Hkv, N/BN, d] in the natural layout so the score kernel reads it as keys.
+template <typename T>
+__global__ __launch_bounds__(256) void pool_blocks_kernel(const T *__restrict__ K, float *__restrict__ kbar,
+                                                          Geometry g, int64_t total) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int k = (int)(gid % g.d);
+    const int64_t blk = gid / g.d;  // (b*Hkv + kvh)*(N/BN) + c
+    const T *src = K + blk * g.BN * g.d + k;
+    float sum = 0.0f;
+    for (int r = 0; r < g.BN; ++r) sum = sum + widen<T>(src[(int64_t)r * g.d]);
+    kbar[gid] = sum * (1.0f / (float)g.BN);
+}
+
 constexpr int SCORE_KEYS = 256;   // keys per workgroup (one per thread)
 constexpr int SCORE_ILP = 4;      // pairs evaluated together (independent fma chains)
 
@@ -231,6 +247,18 @@ hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, float *qse
     int64_t stotal = (int64_t)g.B * g.Hq * g.nseg * g.d;
     hipLaunchKernelGGL(segpool_kernel, dim3((unsigned)((stotal + 255) / 256)), dim3(256), 0, stream,
                        qbar, qseg, g, stotal);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_blocks(const Geometry &g, const void *K, float *kbar, hipStream_t stream) {
+    const int64_t total = (int64_t)g.B * g.Hkv * (g.N / g.BN) * g.d;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (g.dtype == 1)
+        hipLaunchKernelGGL(pool_blocks_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const __bf16 *>(K), kbar, g, total);
+    else
+        hipLaunchKernelGGL(pool_blocks_kernel<float>, dim3(blocks), dim3(256), 0, stream,
+                           reinterpret_cast<const float *>(K), kbar, g, total);
     return hipGetLastError();
 }
 

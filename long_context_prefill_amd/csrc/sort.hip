@@ -28,6 +28,8 @@
 //      A range larger than the LDS capacity (heavily repeated or clustered
 //      scores) is queued and sorted afterwards by one workgroup with LSD
 //      passes through global scratch, chunk by chunk in order: slower, exact.
+// When no list is longer than the LDS capacity (block lists, short sequences)
+// one workgroup sorts each whole list in LDS and no workspace is used.
 #include "s2o_internal.h"
 
 #include <math.h>
@@ -370,9 +372,10 @@ __device__ inline uint32_t block_or(uint32_t x, uint32_t *sh) {
 // Sorts the m <= R*THREADS entries of one range in LDS and writes their
 // positions: stable 8-bit LSD passes on the key relative to the range minimum,
 // only over the bytes that vary.  Padding entries (rel = all ones) stay last.
-template <int R>
-__device__ __forceinline__ void sort_in_lds(const u32x2 *__restrict__ in, int32_t *__restrict__ out, int m, uint32_t *skey,
-                            int32_t *spos, int (*cnt)[NB], int *dtot, uint32_t *red) {
+// load(i) gives entry i as (key, position).
+template <int R, typename Load>
+__device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out, int m, uint32_t *skey,
+                                            int32_t *spos, int (*cnt)[NB], int *dtot, uint32_t *red) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wbase = wave * R * 64 + lane;
     uint32_t rel[R];
@@ -385,7 +388,7 @@ __device__ __forceinline__ void sort_in_lds(const u32x2 *__restrict__ in, int32_
         u32x2 pr;
         pr.x = 0xFFFFFFFFu;
         pr.y = 0;
-        if (i < m) pr = in[i];
+        if (i < m) pr = load(i);
         rel[r] = pr.x;
         pos[r] = (int32_t)pr.y;
         kmin = min(kmin, pr.x);
@@ -463,9 +466,42 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
     }
     const u32x2 *in = pairs + L.off + rs;
     int32_t *out = idx + L.off + rs;
+    auto load = [in](int i) { return in[i]; };
     switch ((m + THREADS - 1) / THREADS) {  // one instantiation per round count
 #define S2O_SORT_CASE(R) \
-    case R: sort_in_lds<R>(in, out, m, skey, spos, cnt, dtot, red); break;
+    case R: sort_in_lds<R>(load, out, m, skey, spos, cnt, dtot, red); break;
+        S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
+        S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
+        S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
+        S2O_SORT_CASE(13) S2O_SORT_CASE(14) S2O_SORT_CASE(15) S2O_SORT_CASE(16)
+#undef S2O_SORT_CASE
+        default: break;
+    }
+}
+
+// Short lists (every list at most CAP entries, e.g. block lists): one
+// workgroup sorts a whole list in LDS straight from the scores.
+__global__ __launch_bounds__(THREADS, 4) void list_sort_kernel(const float *__restrict__ scores,
+                                                               int32_t *__restrict__ idx, Geometry g) {
+    __shared__ uint32_t skey[CAP];
+    __shared__ int32_t spos[CAP];
+    __shared__ int cnt[NWAVES][NB];
+    __shared__ int dtot[NB];
+    __shared__ uint32_t red[NWAVES];
+    const ListRef L = list_ref(g, blockIdx.x);
+    const int m = (int)L.len;
+    if (m == 0) return;
+    const float *s = scores + L.off;
+    int32_t *out = idx + L.off;
+    auto load = [s](int i) {
+        u32x2 pr;
+        pr.x = desc_key(s[i]);
+        pr.y = (uint32_t)i;
+        return pr;
+    };
+    switch ((m + THREADS - 1) / THREADS) {
+#define S2O_SORT_CASE(R) \
+    case R: sort_in_lds<R>(load, out, m, skey, spos, cnt, dtot, red); break;
         S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
         S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
         S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
@@ -562,6 +598,10 @@ int block_elems(const Geometry &g) {
     return e > MAX_BLOCK ? MAX_BLOCK : e;
 }
 
+// Longest list: the last segment's history.
+int64_t max_list_len(const Geometry &g) { return (int64_t)(g.nseg - 1) * g.S; }
+bool short_lists(const Geometry &g) { return max_list_len(g) <= CAP; }
+
 int range_chunk(const Geometry &g) {
     const int e = block_elems(g);
     return e < MAX_CHUNK ? e : MAX_CHUNK;
@@ -626,11 +666,18 @@ hipError_t run_sort(const Geometry &g, const float *scores, int32_t *idx, const 
 
 }  // namespace
 
-size_t sort_workspace_bytes(const Geometry &g) { return carve(g, nullptr).bytes; }
+size_t sort_workspace_bytes(const Geometry &g) { return short_lists(g) ? 0 : carve(g, nullptr).bytes; }
+
+bool sort_supported(const Geometry &g) { return short_lists(g) || block_elems(g) >= 64; }
 
 hipError_t launch_sort(const Geometry &g, const float *scores, int32_t *idx, void *ws,
                        hipStream_t stream) {
     if (g.list_entries == 0) return hipSuccess;
+    if (short_lists(g)) {
+        const unsigned lists = (unsigned)((int64_t)g.B * g.Hq * lists_per_head(g));
+        hipLaunchKernelGGL(list_sort_kernel, dim3(lists), dim3(THREADS), 0, stream, scores, idx, g);
+        return hipGetLastError();
+    }
     SortWs w = carve(g, ws);
     switch (block_elems(g)) {
         case 4096: return run_sort<4096>(g, scores, idx, w, stream);

@@ -53,7 +53,8 @@ class GpuRun:
         self.w = w
         self.lists = lists
         self.p = gpu_problem(w, seg_len, lists)
-        self.po = oracle.problem_from_workload(w, seg_len, per_segment=(lists == "segment"))
+        self.po = oracle.problem_from_workload(w, seg_len, per_segment=lists.startswith("segment"),
+                                               block_lists=lists.endswith("blocks"))
         self.x = x
         self.q, self.k, self.v = (to_device(x[n]) for n in ("q", "k", "v"))
         say(f"{w.name}: score + build_index ({lists} lists, {s2o.list_entries(self.p)} entries)")
@@ -75,12 +76,12 @@ class GpuRun:
 
     def tile_list(self, b, h, t):
         off = s2o.list_offset(self.p, b, h, t)
-        a = oracle.seg_start(self.po, t)
+        a = oracle.list_len(self.po, t)
         return self.idx[off:off + a].cpu().numpy()
 
     def tile_scores(self, b, h, t):
         off = s2o.list_offset(self.p, b, h, t)
-        a = oracle.seg_start(self.po, t)
+        a = oracle.list_len(self.po, t)
         return self.scores[off:off + a].cpu().numpy()
 
 
@@ -110,7 +111,7 @@ def compare(run: GpuRun, tiles, tau, o_gpu, ex_gpu, check_lists=True):
                sum_abs=0.0, n=0)
     forced = []
     for n, (b, h, t) in enumerate(tiles):
-        a = oracle.seg_start(po, t)
+        a = oracle.list_len(po, t)
         if check_lists and a > 0:
             if not np.array_equal(run.tile_list(b, h, t), res["lists"][n, :a]):
                 rep["list_mismatch"] += 1

@@ -76,18 +76,41 @@ def test_segment_list_layout_matches_oracle_walk(N, S, BM, B, Hq):
                 assert s2o.list_offset(p, b, h, t) == oracle.list_offset(po, b, h, t)
 
 
+@pytest.mark.parametrize("lists", ["tile_blocks", "segment_blocks"])
+@pytest.mark.parametrize("N,S,BM,B,Hq", [(1024, 256, 128, 1, 4), (2048, 512, 64, 2, 3),
+                                         (64 * 63, 384, 64, 1, 2), (131072, 8192, 128, 1, 32)])
+def test_block_list_layout_matches_oracle_walk(N, S, BM, B, Hq, lists):
+    p = base_problem(batch=B, heads_q=Hq, heads_kv=1, seq_len=N, seg_len=S, tile_m=BM, lists=lists)
+    assert s2o.check_problem(p) == 0
+    po = oracle.problem(B, Hq, 1, N, 128, "bf16", S, BM, 64, 1.0, per_segment=lists.startswith("segment"),
+                        block_lists=True)
+    assert s2o.list_entries(p) == oracle.list_entries(po)
+    T = N // BM
+    for b in range(B):
+        for h in {0, Hq - 1}:
+            for t in sorted({0, T // 3, T // 2, T - 1}):
+                assert s2o.list_offset(p, b, h, t) == oracle.list_offset(po, b, h, t)
+
+
 def test_workspace_sizes():
     p = base_problem()
     assert s2o.score_workspace_bytes(p) == 1 * 4 * (1024 // 128) * 128 * 4
-    n = s2o.list_entries(p)
-    assert s2o.build_index_workspace_bytes(p) >= 3 * n * 4
+    # every list fits one workgroup's LDS (at most 4096 entries): sorted in place
+    assert s2o.build_index_workspace_bytes(p) == 0
+    # longer lists: (key, position) pairs and their scratch copy, 16 bytes per entry
+    p = base_problem(seq_len=16384, seg_len=4096)
+    assert s2o.build_index_workspace_bytes(p) >= 16 * s2o.list_entries(p)
+    # block lists: the mean key of every block joins the pooled queries
+    p = base_problem(lists="tile_blocks")
+    assert s2o.score_workspace_bytes(p) == 1 * 4 * 8 * 128 * 4 + 1 * 2 * (1024 // 64) * 128 * 4
+    assert s2o.list_entries(p) == s2o.list_entries(base_problem()) // 64
 
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", 0, INVALID), ("heads_q", 3, INVALID), ("seq_len", 1000, INVALID),
     ("seg_len", 200, INVALID), ("head_dim", 96, UNSUPPORTED), ("tile_m", 256, UNSUPPORTED),
     ("tile_n", 32, UNSUPPORTED), ("dtype", 7, INVALID), ("causal", 2, INVALID),
-    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 2, INVALID)])
+    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 4, INVALID), ("list_granularity", -1, INVALID)])
 def test_problem_validation(field, value, code):
     p = base_problem()
     setattr(p, field, value)
@@ -118,11 +141,14 @@ def test_entry_points_reject_bad_arguments_before_launch():
     # bad tau
     assert L.s2o_attn_fwd(pb, fake, fake, fake, fake, -1e-3, fake, nul, nul) == INVALID
     assert L.s2o_attn_fwd(pb, fake, fake, fake, fake, float("nan"), fake, nul, nul) == INVALID
-    # workspace missing, too small or misaligned
-    need = s2o.build_index_workspace_bytes(p)
-    assert L.s2o_build_index(pb, fake, fake, nul, need, nul) == WORKSPACE
-    assert L.s2o_build_index(pb, fake, fake, fake, need - 1, nul) == WORKSPACE
-    assert L.s2o_build_index(pb, fake, fake, ctypes.c_void_p(0x100080), need, nul) == WORKSPACE
+    # workspace missing, too small or misaligned (lists long enough to need one)
+    pl = base_problem(seq_len=16384, seg_len=4096)
+    plb = ctypes.byref(pl)
+    need = s2o.build_index_workspace_bytes(pl)
+    assert need > 0
+    assert L.s2o_build_index(plb, fake, fake, nul, need, nul) == WORKSPACE
+    assert L.s2o_build_index(plb, fake, fake, fake, need - 1, nul) == WORKSPACE
+    assert L.s2o_build_index(plb, fake, fake, ctypes.c_void_p(0x100080), need, nul) == WORKSPACE
     assert L.s2o_score(pb, fake, fake, fake, fake, s2o.score_workspace_bytes(p) - 4, nul) == WORKSPACE
     # causal = 0 is dense-only
     pc = base_problem(causal=False)

@@ -374,3 +374,64 @@ def test_build_index_crafted_scores(kind, lists):
     idx = s2o.s2o_build_index(p, torch.from_numpy(sc).cuda())
     torch.cuda.synchronize()
     assert np.array_equal(idx.cpu().numpy(), oracle.lists_all(po, sc))
+
+
+# ------------------------------------------------------------- block lists ---
+# Entries are blocks of BN keys scored by their mean key; pass-2 chunk c is the
+# c-th listed block (the block-granularity counterpart of the method).
+
+@pytest.mark.parametrize("lists", ["tile_blocks", "segment_blocks"])
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_bf16_block_lists_every_tile(case, lists):
+    name, B, Hq, Hkv, N, d, BM, S, structure = case
+    w = synth.custom_workload(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", tile_m=BM, tile_n=64,
+                              seg_len=S, structure=structure, n_stripes=max(N // 100, 4),
+                              seed=900 + N + d, name=name)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists=lists)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    for tau in (0.0, 1e-3, 3e-2):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, all_tiles(w), tau, o, ex, check_lists=False), "bf16")
+
+
+def test_tiny_f32_block_lists():
+    w = synth.WORKLOADS["tiny_f32_n2048_s512"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="tile_blocks")
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    for tau in (1e-3, 0.0):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, all_tiles(w), tau, o, ex), "f32")
+
+
+def test_llama8b_16k_block_lists():
+    w = synth.WORKLOADS["llama8b_n16k"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="tile_blocks")
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    tiles = sample_tiles(w, heads=(0, 9, 18, 27), n_random=16, seed=7)
+    for tau in (1e-2, 1e-3):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex, check_lists=False), "bf16")
+    o, ex = run.attn(0.0)
+    od = run.dense()
+    d = (o.float() - od.float()).abs()
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_128k_block_lists_sampled():
+    w = synth.WORKLOADS["llama8b_n128k"]
+    say("generating llama8b_n128k inputs")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="tile_blocks")
+    tiles = sample_tiles(w, heads=(5, 22), n_random=8, seed=8)
+    o, ex = run.attn(1e-3)
+    assert_report(compare(run, tiles, 1e-3, o, ex, check_lists=True), "bf16")

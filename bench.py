@@ -11,7 +11,10 @@ dense_attn_fwd over all B*Hq*N*d elements, fp32), unless --tau is given.
 
 The headline uses one index list per query tile.  The same measurement with
 one list per segment (shared by the segment's tiles) is reported under
-"segment_lists".
+"segment_lists", and with blocks of 64 keys as list entries (the
+block-granularity counterpart the method is compared with) under
+"block_lists".  "ranking_study" measures, on sampled tiles, how well each
+list's order matches every row's true attention order.
 
 Prints one JSON line (rank 0, one GPU).  Extra fields: per-phase times, the
 dense kernel's time, compute density, MSE, the MFMA roofline of the attention
@@ -57,6 +60,9 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--tile-lists-only", action="store_true",
                     help="skip the per-segment-list measurement")
+    ap.add_argument("--modes", default="segment,tile_blocks",
+                    help="list forms measured besides the headline per-tile lists")
+    ap.add_argument("--no-ranking-study", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for profiles)")
     return ap.parse_args()
@@ -76,6 +82,51 @@ def traffic_figure():
     if rec.get("kernel_source_sha256_16") != source_hash(ATTN_SOURCE):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles):
+    """How well a tile's list order matches each row's true attention order.
+
+    For every sampled tile (b, h, t) with history a > 0, E is the set of history
+    keys the tile executed (the first n*BN keys the list visits, n = executed
+    pass-2 chunks; a block entry stands for its BN keys).  For every row i with
+    logits x_ij = scale * q_i . k_j over the history keys j < a:
+      overlap   |E intersect top_i| / |E|, top_i = the |E| keys of largest x_ij
+      mass      sum_{j in E} e^x_ij / sum_{j in top_i} e^x_ij  (1 = the best set of that size)
+      coverage  sum_{j in E} e^x_ij / sum_{j < a} e^x_ij        (history mass executed)
+      spearman  rank correlation between list position and -x_ij
+    averaged over rows and tiles.  Plain numpy in fp32 from the bf16 inputs.
+    """
+    from long_context_prefill_amd import synth
+    BN = w.tile_n
+    G = w.Hq // w.Hkv
+    acc = {"overlap": [], "mass": [], "coverage": [], "spearman": []}
+    for (b, h, t) in tiles:
+        a = (t * w.tile_m // w.seg_len) * w.seg_len
+        if a == 0:
+            continue
+        n = int(exec_tiles[b, h, t]) - ((t + 1) * w.tile_m - a) // BN
+        off = offsets(b, h, t)
+        ent = idx[off:off + (a // BN if lists.endswith("blocks") else a)]
+        order = (ent[:, None] * BN + np.arange(BN)).ravel() if lists.endswith("blocks") else ent
+        widen = synth.f32_from_bf16_bits if w.dtype == "bf16" else (lambda z: np.asarray(z, np.float32))
+        q = widen(x["q"][b, h, t * w.tile_m:(t + 1) * w.tile_m])
+        k = widen(x["k"][b, h // G, :a])
+        xl = (q @ k.T) * np.float32(w.scale)                       # [BM, a]
+        ex = np.exp(xl - xl.max(axis=1, keepdims=True))
+        E = order[:n * BN]
+        in_e = np.zeros(a, dtype=bool)
+        in_e[E] = True
+        top = np.argpartition(-xl, n * BN - 1, axis=1)[:, :n * BN]
+        acc["overlap"].append(in_e[top].mean())
+        acc["mass"].append(float(np.mean(ex[:, E].sum(axis=1) / np.take_along_axis(ex, top, 1).sum(axis=1))))
+        acc["coverage"].append(float(np.mean(ex[:, E].sum(axis=1) / ex.sum(axis=1))))
+        pos = np.empty(a, dtype=np.float64)
+        pos[order] = np.arange(a)
+        rk = np.argsort(np.argsort(-xl, axis=1), axis=1).astype(np.float64)
+        pc, rc = pos - pos.mean(), rk - rk.mean(axis=1, keepdims=True)
+        acc["spearman"].append(float(np.mean((rc @ pc) / (np.sqrt((rc ** 2).sum(axis=1)) * np.sqrt((pc ** 2).sum())))))
+    return {k: round(float(np.mean(v)), 4) for k, v in acc.items()} | {"tiles": len(acc["mass"])}
 
 
 def cpu_baseline(w, x, tau, exec_gpu, n_tiles):
@@ -192,12 +243,18 @@ def main():
         score_ms, sort_ms, attn_ms = (float(np.mean(ph[:, j])) for j in range(3))
         executed = int(exec_tiles.sum())
         achieved = executed * flop_per_tile / (attn_ms * 1e-3) / 1e12
+        study = None
+        if not args.no_ranking_study:
+            log(f"[{lists} lists] ranking study on {len(study_tiles)} tiles")
+            study = ranking_study(w, x, lists, idx.cpu().numpy(),
+                                  lambda b_, h_, t_: s2o.list_offset(p, b_, h_, t_),
+                                  exec_tiles.cpu().numpy(), study_tiles)
         log(f"[{lists} lists] step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index "
             f"{sort_ms:.2f} + attn {attn_ms:.2f}")
         res = {"tau": tau, "ms_per_step": ms_per_step, "score_ms": score_ms, "sort_ms": sort_ms,
                "attn_ms": attn_ms, "executed": executed, "density": executed / dense_tiles,
                "mse": chosen["mse"], "rel_mse": chosen["rel_mse"], "achieved": achieved,
-               "sweep": sweep, "exec_tiles": exec_tiles.cpu().numpy()}
+               "sweep": sweep, "exec_tiles": exec_tiles.cpu().numpy(), "study": study}
         del scores, idx, ws_score, ws_sort, out, exec_tiles
         torch.cuda.empty_cache()
         return res
@@ -211,8 +268,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    rng_s = np.random.default_rng(777)
+    study_tiles = [(0, int(rng_s.integers(w.Hq)), int(rng_s.integers(w.seg_len // w.tile_m, T)))
+                   for _ in range(12)]
     main = run_mode("tile", args.steps, args.warmup, args.tau)
-    seg = None if args.tile_lists_only else run_mode("segment", args.steps, args.warmup, args.tau)
+    extra = {} if args.tile_lists_only else {
+        m: run_mode(m, args.steps, args.warmup, args.tau) for m in args.modes.split(",") if m}
 
     rec = {
         "metric": METRIC, "value": round(main["ms_per_step"], 3), "unit": "ms", "n_gpus": 1,
@@ -241,17 +302,22 @@ def main():
                      "traffic": traffic_figure(), "kernel": "s2o_attn_fwd",
                      "work": f"{main['executed']} executed 128x64 tiles x {flop_per_tile:.0f} flop"},
     }
-    if seg is not None:
-        rec["segment_lists"] = {
-            "ms_per_step": round(seg["ms_per_step"], 3), "tau": seg["tau"],
-            "phases_ms": {"s2o_score": round(seg["score_ms"], 3),
-                          "s2o_build_index": round(seg["sort_ms"], 3),
-                          "s2o_attn_fwd": round(seg["attn_ms"], 3)},
-            "speedup_vs_dense": round(dense_ms / seg["ms_per_step"], 3),
-            "density": round(seg["density"], 4), "mse_vs_dense": seg["mse"],
-            "rel_mse_vs_dense": seg["rel_mse"],
-            "mfma_pct_executed_tiles": round(100.0 * seg["achieved"] / BF16_MFMA_PEAK_TFLOPS, 2),
-            "tau_sweep": seg["sweep"]}
+    names = {"segment": "segment_lists", "tile_blocks": "block_lists",
+             "segment_blocks": "segment_block_lists"}
+    for m, r in extra.items():
+        rec[names.get(m, m + "_lists")] = {
+            "ms_per_step": round(r["ms_per_step"], 3), "tau": r["tau"],
+            "phases_ms": {"s2o_score": round(r["score_ms"], 3),
+                          "s2o_build_index": round(r["sort_ms"], 3),
+                          "s2o_attn_fwd": round(r["attn_ms"], 3)},
+            "speedup_vs_dense": round(dense_ms / r["ms_per_step"], 3),
+            "density": round(r["density"], 4), "mse_vs_dense": r["mse"],
+            "rel_mse_vs_dense": r["rel_mse"],
+            "mfma_pct_executed_tiles": round(100.0 * r["achieved"] / BF16_MFMA_PEAK_TFLOPS, 2),
+            "tau_sweep": r["sweep"]}
+    if not args.no_ranking_study:
+        rec["ranking_study"] = {"tiles": "12 seeded tiles with history, at each form's tau",
+                                "tile": main["study"]} | {m: r["study"] for m, r in extra.items()}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         rec["cpu_baseline"] = cpu_baseline(w, x, main["tau"], main["exec_tiles"], args.cpu_tiles)

@@ -1,0 +1,55 @@
+"""CPU checks of the ranking study bench.py reports (no GPU): on inputs whose
+true attention order is known, the study's figures take their extreme values."""
+
+import numpy as np
+
+import bench
+from long_context_prefill_amd import synth
+
+
+def _problem(N=512, d=16, BM=64, BN=64, S=256):
+    w = synth.custom_workload(B=1, Hq=1, Hkv=1, N=N, d=d, dtype="f32", tile_m=BM, tile_n=BN,
+                              seg_len=S, structure="uniform", seed=3)
+    rng = np.random.default_rng(0)
+    # every query row is the same vector, so all rows of a tile share one key order
+    qrow = rng.standard_normal(d).astype(np.float32)
+    k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    q = np.tile(qrow, (1, 1, N, 1)).astype(np.float32)
+    return w, {"q": q, "k": k, "v": k}, qrow
+
+
+def _run(order_fn, n_chunks, lists="tile"):
+    w, x, qrow = _problem()
+    T = w.N // w.tile_m
+    t = T - 1
+    a = (t * w.tile_m // w.seg_len) * w.seg_len
+    true_order = np.argsort(-(x["k"][0, 0, :a] @ qrow), kind="stable").astype(np.int32)
+    ent = order_fn(true_order, a, w.tile_n)
+    idx = np.zeros(1 << 12, np.int32)
+    idx[:len(ent)] = ent
+    exec_tiles = np.zeros((1, 1, T), np.int32)
+    exec_tiles[0, 0, t] = ((t + 1) * w.tile_m - a) // w.tile_n + n_chunks
+    return bench.ranking_study(w, x, lists, idx, lambda b, h, tt: 0, exec_tiles, [(0, 0, t)])
+
+
+def test_true_order_scores_one():
+    r = _run(lambda o, a, bn: o, n_chunks=2)
+    assert r["tiles"] == 1
+    assert r["overlap"] == 1.0 and r["mass"] == 1.0 and r["spearman"] == 1.0
+    assert 0.0 < r["coverage"] < 1.0
+
+
+def test_reversed_order():
+    r = _run(lambda o, a, bn: o[::-1].copy(), n_chunks=1)
+    assert r["overlap"] == 0.0 and r["mass"] < 0.25 and r["spearman"] == -1.0
+
+
+def test_all_chunks_cover_everything():
+    r = _run(lambda o, a, bn: o[::-1].copy(), n_chunks=256 // 64)
+    assert r["coverage"] == 1.0 and r["overlap"] == 1.0 and r["mass"] == 1.0
+
+
+def test_block_entries_expand_to_their_keys():
+    # blocks in ascending order with every chunk executed: the whole history is covered
+    r = _run(lambda o, a, bn: np.arange(a // bn, dtype=np.int32), n_chunks=256 // 64, lists="tile_blocks")
+    assert r["coverage"] == 1.0 and r["overlap"] == 1.0

@@ -591,17 +591,26 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     const __bf16 *Kp = reinterpret_cast<const __bf16 *>(a.k) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
     const __bf16 *Vp = reinterpret_cast<const __bf16 *>(a.v) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
 
-    auto chunk_row = [&](int k, int p) -> int {
-        if (k < n1) return base1 + k * BN + p;
-        return g.blocks ? list[k - n1] * BN + p : list[(k - n1) * BN + p];
-    };
     // slot q = (wave*INSTR + i)*64 + lane of a tile: row q / CPR, slot q % CPR
     auto slot_row = [&](int i) { return ((wave * C::INSTR + i) * 64 + lane) / C::CPR; };
     auto slot_col = [&](int i) { return ((wave * C::INSTR + i) * 64 + lane) % C::CPR; };
     int krows[C::INSTR], vrows[C::INSTR];
+    // Key rows this lane moves for chunk k: consecutive keys in pass 1; the
+    // chunk's list entries in pass 2 (for block lists, the BN keys of one
+    // listed block).  The branch is uniform across the workgroup.
     auto fetch_rows = [&](int k, int (&rows)[C::INSTR]) {
+        if (!S2O || k < n1) {
 #pragma unroll
-        for (int i = 0; i < C::INSTR; ++i) rows[i] = chunk_row(k, slot_row(i));
+            for (int i = 0; i < C::INSTR; ++i) rows[i] = base1 + k * BN + slot_row(i);
+        } else if (g.blocks) {
+            const int first = list[k - n1] * BN;
+#pragma unroll
+            for (int i = 0; i < C::INSTR; ++i) rows[i] = first + slot_row(i);
+        } else {
+            const int32_t *entries = list + (int64_t)(k - n1) * BN;
+#pragma unroll
+            for (int i = 0; i < C::INSTR; ++i) rows[i] = entries[slot_row(i)];
+        }
     };
     auto issue_k = [&](int stage, const int (&rows)[C::INSTR]) {
 #pragma unroll

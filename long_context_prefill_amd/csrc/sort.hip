@@ -45,6 +45,8 @@ constexpr int MAX_CHUNK = 2048;  // output positions owned by a range-sort workg
 constexpr int CAP = 4096;        // entries a range-sort workgroup holds in LDS
 constexpr int CAP_ROUNDS = CAP / THREADS;
 constexpr int OVERFLOW_GRID = 1024;  // workgroups draining the overflow queue
+static_assert(THREADS == NB, "the in-LDS passes give each thread one digit");
+static_assert(NWAVES * NB == 4 * THREADS, "counter clear: four per thread");
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -247,11 +249,10 @@ __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restric
                                                           u32x2 *__restrict__ pairs, Geometry g) {
     constexpr int NWV = E >= 256 ? NWAVES : E / 64;  // waves holding entries
     constexpr int ROUNDS = E / (64 * NWV);           // wave w owns [w*E/NWV, (w+1)*E/NWV)
-    __shared__ int cnt[NWAVES][NB];  // per-wave digit counters, then wave offsets
+    __shared__ int cnt[NWAVES][NB];  // per-wave digit counters, then staging offsets
     __shared__ int dstart[NB];       // first staged position of each digit
-    __shared__ int dglob[NB];        // run start of each digit, relative to the block
-    __shared__ uint32_t skey[E];
-    __shared__ int32_t spos[E];
+    __shared__ int dglob[NB];        // run start of each digit relative to the block, minus dstart
+    __shared__ u32x2 stage[E];       // (key, position) sorted by digit
     __shared__ uint8_t sdig[E];
     __shared__ float sh[2];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -290,23 +291,27 @@ __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restric
     __syncthreads();
     scan256(dstart);
     __syncthreads();
+    // fold the digit starts into the per-wave offsets and the run starts, so
+    // each entry needs one lookup on the way in and one on the way out
+    for (int v = tid; v < NB; v += THREADS) {
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) cnt[w][v] += dstart[v];
+        dglob[v] -= dstart[v];
+    }
+    __syncthreads();
     if (wave < NWV) {
 #pragma unroll
         for (int r = 0; r < ROUNDS; ++r) {
-            const int p = dstart[dig[r]] + cnt[wave][dig[r]] + rank[r];
-            skey[p] = desc_key(x[r]);
-            spos[p] = pos0 + wave * (E / NWV) + 64 * r + lane;
+            const int p = cnt[wave][dig[r]] + rank[r];
+            u32x2 pr;
+            pr.x = desc_key(x[r]);
+            pr.y = (uint32_t)(pos0 + wave * (E / NWV) + 64 * r + lane);
+            stage[p] = pr;
             sdig[p] = (uint8_t)dig[r];
         }
     }
     __syncthreads();
-    for (int i = tid; i < E; i += THREADS) {
-        const int d = sdig[i];
-        u32x2 pr;
-        pr.x = skey[i];
-        pr.y = (uint32_t)spos[i];
-        pairs[base + dglob[d] + (i - dstart[d])] = pr;
-    }
+    for (int i = tid; i < E; i += THREADS) pairs[base + dglob[sdig[i]] + i] = stage[i];
 }
 
 // Stable rank of one chunk (striped: entry w*rounds*64 + r*64 + lane) by the
@@ -374,8 +379,8 @@ __device__ inline uint32_t block_or(uint32_t x, uint32_t *sh) {
 // only over the bytes that vary.  Padding entries (rel = all ones) stay last.
 // load(i) gives entry i as (key, position).
 template <int R, typename Load>
-__device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out, int m, uint32_t *skey,
-                                            int32_t *spos, int (*cnt)[NB], int *dtot, uint32_t *red) {
+__device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out, int m, u32x2 *stage,
+                                            int (*cnt)[NB], uint32_t *red) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wbase = wave * R * 64 + lane;
     uint32_t rel[R];
@@ -405,23 +410,63 @@ __device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 8 * pass;
         if (((span >> shift) & 0xFFu) == 0) continue;  // digit constant in the range
-        rank_chunk<R>(rel, rank, R, shift, cnt, dtot);
-        scan256(dtot);
+        // per-wave digit counters: zero, count with stable in-wave ranks
+        *reinterpret_cast<int4 *>(&cnt[0][0] + 4 * threadIdx.x) = int4{0, 0, 0, 0};
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint32_t d = (rel[r] >> shift) & 0xFFu;
-            const int p = dtot[d] + cnt[wave][d] + rank[r];
-            skey[p] = rel[r];
-            spos[p] = pos[r];
+            const uint64_t peers = match_digit(d);
+            const int before = cnt[wave][d];
+            rank[r] = before + __popcll(peers & lanemask_lt());
+            if ((peers & lanemask_lt()) == 0) cnt[wave][d] = before + __popcll(peers);
+            __builtin_amdgcn_sched_barrier(0);  // one round at a time: bounds register use
         }
         __syncthreads();
+        // thread v = digit v: wave offsets inside the digit, then the digit's
+        // start (block-wide exclusive scan: in-wave shuffles, then wave totals)
+        {
+            const int v = threadIdx.x;
+            int tot = 0;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) {
+                const int c = cnt[w][v];
+                cnt[w][v] = tot;
+                tot += c;
+            }
+            int incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int x = __shfl_up(incl, o);
+                if (lane >= o) incl += x;
+            }
+            if (lane == 63) red[wave] = (uint32_t)incl;
+            __syncthreads();
+            int base = 0;
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) base += w < wave ? (int)red[w] : 0;
+            const int start = base + incl - tot;  // first staged position of digit v
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) cnt[w][v] += start;
+        }
+        __syncthreads();
+        // stage (key, position) pairs sorted by the digit: one read, one 8-byte write
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            rel[r] = skey[wbase + 64 * r];
-            pos[r] = spos[wbase + 64 * r];
+            const uint32_t d = (rel[r] >> shift) & 0xFFu;
+            u32x2 pr;
+            pr.x = rel[r];
+            pr.y = (uint32_t)pos[r];
+            stage[cnt[wave][d] + rank[r]] = pr;
         }
         __syncthreads();
+        // (the next pass writes the stage only after its own barriers)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const u32x2 pr = stage[wbase + 64 * r];
+            rel[r] = pr.x;
+            pos[r] = (int32_t)pr.y;
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -444,10 +489,8 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
                                                                 Overflow *__restrict__ queue,
                                                                 int32_t *__restrict__ queue_len,
                                                                 Geometry g, int E) {
-    __shared__ uint32_t skey[CAP];
-    __shared__ int32_t spos[CAP];
+    __shared__ u32x2 stage[CAP];
     __shared__ int cnt[NWAVES][NB];
-    __shared__ int dtot[NB];
     __shared__ uint32_t red[NWAVES];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t e0 = (int64_t)blockIdx.x * C;
@@ -469,7 +512,7 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
     auto load = [in](int i) { return in[i]; };
     switch ((m + THREADS - 1) / THREADS) {  // one instantiation per round count
 #define S2O_SORT_CASE(R) \
-    case R: sort_in_lds<R>(load, out, m, skey, spos, cnt, dtot, red); break;
+    case R: sort_in_lds<R>(load, out, m, stage, cnt, red); break;
         S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
         S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
         S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
@@ -483,10 +526,8 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
 // workgroup sorts a whole list in LDS straight from the scores.
 __global__ __launch_bounds__(THREADS, 4) void list_sort_kernel(const float *__restrict__ scores,
                                                                int32_t *__restrict__ idx, Geometry g) {
-    __shared__ uint32_t skey[CAP];
-    __shared__ int32_t spos[CAP];
+    __shared__ u32x2 stage[CAP];
     __shared__ int cnt[NWAVES][NB];
-    __shared__ int dtot[NB];
     __shared__ uint32_t red[NWAVES];
     const ListRef L = list_ref(g, blockIdx.x);
     const int m = (int)L.len;
@@ -501,7 +542,7 @@ __global__ __launch_bounds__(THREADS, 4) void list_sort_kernel(const float *__re
     };
     switch ((m + THREADS - 1) / THREADS) {
 #define S2O_SORT_CASE(R) \
-    case R: sort_in_lds<R>(load, out, m, skey, spos, cnt, dtot, red); break;
+    case R: sort_in_lds<R>(load, out, m, stage, cnt, red); break;
         S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
         S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
         S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)

@@ -50,7 +50,8 @@ class Problem(ctypes.Structure):
                 ("N", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("seg_len", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("scale", ctypes.c_double),
-                ("per_segment", ctypes.c_int32), ("block_lists", ctypes.c_int32)]
+                ("per_segment", ctypes.c_int32), ("block_lists", ctypes.c_int32),
+                ("qperm", ctypes.c_int32)]
 
 
 _lib = None
@@ -72,8 +73,12 @@ def _load():
             "oracle_list_entries": (i64, [P]),
             "oracle_list_len": (i64, [P, ctypes.c_int]),
             "oracle_pool_block": (None, [P, vp, ctypes.c_int, ctypes.c_int, i64, vp]),
-            "oracle_pool": (None, [P, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
-            "oracle_rep_query": (None, [P, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
+            "oracle_pool": (None, [P, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
+            "oracle_rep_query": (None, [P, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
+            "oracle_guide": (None, [P, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
+            "oracle_query_scores": (None, [P, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
+            "oracle_tile_rows": (None, [P, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
+            "oracle_query_list_offset": (i64, [P, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
             "oracle_score_tile": (None, [P, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]),
             "oracle_order": (None, [vp, i64, vp]),
             "oracle_attn_tile": (i32, [P, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -95,18 +100,20 @@ def _load():
 
 
 def problem(B, Hq, Hkv, N, d, dtype, seg_len, tile_m, tile_n, scale, per_segment=False,
-            block_lists=False) -> Problem:
+            block_lists=False, qperm=False) -> Problem:
     """dtype: "f32" (float32 arrays) or "bf16" (uint16 bit-pattern arrays).
     per_segment: one list per segment (shared by its tiles) instead of per tile.
-    block_lists: list entries are blocks of tile_n keys instead of keys."""
+    block_lists: list entries are blocks of tile_n keys instead of keys.
+    qperm: query rows ordered within each segment by a guide score (Q_perm)."""
     return Problem(B, Hq, Hkv, N, d, 0 if dtype == "f32" else 1, seg_len, tile_m, tile_n,
-                   float(scale), 1 if per_segment else 0, 1 if block_lists else 0)
+                   float(scale), 1 if per_segment else 0, 1 if block_lists else 0, 1 if qperm else 0)
 
 
-def problem_from_workload(w, seg_len=None, per_segment=False, block_lists=False) -> Problem:
+def problem_from_workload(w, seg_len=None, per_segment=False, block_lists=False,
+                          qperm=False) -> Problem:
     return problem(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype,
                    w.seg_len if seg_len is None else seg_len, w.tile_m, w.tile_n, w.scale,
-                   per_segment, block_lists)
+                   per_segment, block_lists, qperm)
 
 
 def _ptr(a):
@@ -156,17 +163,53 @@ def num_threads():
     return _load().oracle_num_threads()
 
 
-def pool(p, Q, b, h, t):
+def _kptr(p, K):
+    if K is None:
+        if p.qperm:
+            raise ValueError("Q_perm needs K (the segment guide is the mean key)")
+        return None
+    return _ptr(_check(K, p, "K"))
+
+
+def pool(p, Q, b, h, t, K=None):
     out = np.empty(p.d, dtype=np.float32)
-    _load().oracle_pool(ctypes.byref(p), _ptr(_check(Q, p, "Q")), b, h, t, _ptr(out))
+    _load().oracle_pool(ctypes.byref(p), _ptr(_check(Q, p, "Q")), _kptr(p, K), b, h, t, _ptr(out))
     return out
 
 
-def rep_query(p, Q, b, h, t):
+def rep_query(p, Q, b, h, t, K=None):
     """The representative query of the list tile t uses (tile mean or segment mean)."""
     out = np.empty(p.d, dtype=np.float32)
-    _load().oracle_rep_query(ctypes.byref(p), _ptr(_check(Q, p, "Q")), b, h, t, _ptr(out))
+    _load().oracle_rep_query(ctypes.byref(p), _ptr(_check(Q, p, "Q")), _kptr(p, K), b, h, t, _ptr(out))
     return out
+
+
+def guide(p, K, b, g, s):
+    """Q_perm guide of segment s for KV head g (the segment's mean key)."""
+    out = np.empty(p.d, dtype=np.float32)
+    _load().oracle_guide(ctypes.byref(p), _ptr(_check(K, p, "K")), b, g, s, _ptr(out))
+    return out
+
+
+def query_scores(p, Q, K, b, h, s):
+    """Q_perm importance scores of the rows of segment s, in row order."""
+    a = s * p.seg_len
+    n = min(p.N, a + p.seg_len) - a
+    out = np.empty(n, dtype=np.float32)
+    _load().oracle_query_scores(ctypes.byref(p), _ptr(_check(Q, p, "Q")), _ptr(_check(K, p, "K")),
+                                b, h, s, _ptr(out))
+    return out
+
+
+def tile_rows(p, Q, K, b, h, t):
+    """Absolute rows of query tile t, in tile order."""
+    out = np.empty(p.tile_m, dtype=np.int64)
+    _load().oracle_tile_rows(ctypes.byref(p), _ptr(_check(Q, p, "Q")), _kptr(p, K), b, h, t, _ptr(out))
+    return out
+
+
+def query_list_offset(p, b, h, s):
+    return _load().oracle_query_list_offset(ctypes.byref(p), b, h, s)
 
 
 def score_tile(p, Q, K, b, h, t):
@@ -225,7 +268,9 @@ def attn_tiles(p, Q, K, V, tiles, tau, lists=None, force_n=None, want_lists=Fals
                           _ptr(_check(V, p, "V")), _ptr(tiles), n, _ptr(lists), float(tau),
                           _ptr(fn), _ptr(out), _ptr(n_exec), _ptr(chunks), _ptr(gstar),
                           max_chunks, _ptr(lout), max_list)
-    res = {"out": out, "n_exec": n_exec, "chunks": chunks, "gstar": gstar}
+    res = {"out": out, "n_exec": n_exec, "chunks": chunks, "gstar": gstar,
+           "rows": np.stack([tile_rows(p, Q, K, int(b), int(h), int(t)) for b, h, t in tiles])
+           if p.qperm else None}
     if want_lists:
         res["lists"] = lout
     return res

@@ -44,6 +44,19 @@
  *              the block-granularity counterpart the pages compare against
  *              ([ABS] and [GIST] contrast token-level ordering with block-level
  *              sparse attention).
+ *   query permutation (optional, Q_perm): inside each segment the query rows
+ *              are ordered by a coarse importance score against a shared
+ *              guide vector ([GIST] Classement par Segment, Q_perm: queries
+ *              reordered within a segment to favour those likely to produce
+ *              salient horizontal bands).  The guide is the segment's mean key
+ *              (fp32 sum of its key rows in ascending order, times fl(1/rows));
+ *              a row's score is the same fma chain as above; rows are sorted by
+ *              score descending, ties to the lower row.  Query tile t of the
+ *              segment is then rows order[(t - first tile)*BM ...] of that
+ *              order; its representative is the fp32 sum of those rows in that
+ *              order times 1/BM; pass 1 runs each row over its own causal
+ *              window [a_t, i] (key tiles up to the tile's last row); outputs
+ *              go back to the rows' own positions.
  *   order      the list: history keys (or blocks) sorted by score descending,
  *              ties to the lower index ([GIST] KV_perm: indices form a global
  *              logical map).
@@ -84,6 +97,7 @@ typedef struct {
     double scale;
     int32_t per_segment; /* 0: one list per query tile; 1: one list per segment */
     int32_t block_lists; /* 0: entries are keys; 1: entries are blocks of tile_n keys */
+    int32_t qperm;       /* 1: query rows permuted within each segment (Q_perm) */
 } oracle_problem;
 
 /* ---- element access ------------------------------------------------------ */
@@ -154,30 +168,97 @@ int64_t oracle_list_offset(const oracle_problem *p, int b, int h, int t) {
 }
 
 int64_t oracle_list_entries(const oracle_problem *p) {
-    return (int64_t)p->B * p->Hq * per_head_entries(p);
+    int64_t n = (int64_t)p->B * p->Hq * per_head_entries(p);
+    if (p->qperm) n += (int64_t)p->B * p->Hq * p->N; /* the query orders, after every key list */
+    return n;
+}
+
+/* Q_perm: offset of the query order of segment s of (b, h): after all key
+ * lists, one run of N entries per (b, h), segment by segment; entries are
+ * row numbers relative to the segment start. */
+int64_t oracle_query_list_offset(const oracle_problem *p, int b, int h, int s) {
+    return (int64_t)p->B * p->Hq * per_head_entries(p) + ((int64_t)b * p->Hq + h) * p->N +
+           (int64_t)s * p->seg_len;
+}
+
+static int64_t seg_rows(const oracle_problem *p, int s) {
+    int64_t a = (int64_t)s * p->seg_len, e = a + p->seg_len;
+    return (e > p->N ? p->N : e) - a;
 }
 
 /* ---- estimator: pool and score ------------------------------------------- */
 
-/* Representative query of tile t: the mean of its BM rows (fp32 sum in
- * ascending row order, then an exact power-of-two scaling; BM must be a power
- * of two). */
-void oracle_pool(const oracle_problem *p, const void *Q, int b, int h, int t, float *qbar) {
-    float inv = 1.0f / (float)p->tile_m; /* exact for powers of two */
+/* ---- query permutation (Q_perm) ------------------------------------------ */
+
+/* Guide of segment s for KV head g: the segment's mean key. */
+void oracle_guide(const oracle_problem *p, const void *K, int b, int g, int s, float *guide) {
+    int64_t a = (int64_t)s * p->seg_len, n = seg_rows(p, s);
+    float inv = 1.0f / (float)n;
     for (int k = 0; k < p->d; ++k) {
         float sum = 0.0f;
-        for (int r = 0; r < p->tile_m; ++r)
-            sum = sum + widen(Q, p->dtype, q_index(p, b, h, (int64_t)t * p->tile_m + r, k));
+        for (int64_t j = 0; j < n; ++j) sum = sum + widen(K, p->dtype, kv_index(p, b, g, a + j, k));
+        guide[k] = sum * inv;
+    }
+}
+
+/* Importance scores of the query rows of segment s of head h (fma chain
+ * against the guide, ascending k), in row order. */
+void oracle_query_scores(const oracle_problem *p, const void *Q, const void *K, int b, int h, int s,
+                         float *out) {
+    int g = h / (p->Hq / p->Hkv);
+    int64_t a = (int64_t)s * p->seg_len, n = seg_rows(p, s);
+    float *guide = (float *)malloc(sizeof(float) * p->d);
+    oracle_guide(p, K, b, g, s, guide);
+    for (int64_t i = 0; i < n; ++i) {
+        float acc = 0.0f;
+        for (int k = 0; k < p->d; ++k) acc = fmaf(widen(Q, p->dtype, q_index(p, b, h, a + i, k)), guide[k], acc);
+        out[i] = acc;
+    }
+    free(guide);
+}
+
+void oracle_order(const float *scores, int64_t n, int32_t *list);
+
+/* Rows of tile t (absolute row numbers), in tile order. */
+void oracle_tile_rows(const oracle_problem *p, const void *Q, const void *K, int b, int h, int t,
+                      int64_t *rows) {
+    int64_t row0 = (int64_t)t * p->tile_m;
+    if (!p->qperm) {
+        for (int r = 0; r < p->tile_m; ++r) rows[r] = row0 + r;
+        return;
+    }
+    int s = (int)(oracle_seg_start(p, t) / p->seg_len);
+    int64_t a = (int64_t)s * p->seg_len, n = seg_rows(p, s);
+    float *sc = (float *)malloc(sizeof(float) * n);
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * n);
+    oracle_query_scores(p, Q, K, b, h, s, sc);
+    oracle_order(sc, n, order);
+    for (int r = 0; r < p->tile_m; ++r) rows[r] = a + order[row0 - a + r];
+    free(order);
+    free(sc);
+}
+
+/* Representative query of tile t: the mean of its BM rows (fp32 sum over the
+ * rows in tile order, then an exact power-of-two scaling; BM must be a power
+ * of two). */
+void oracle_pool(const oracle_problem *p, const void *Q, const void *K, int b, int h, int t, float *qbar) {
+    float inv = 1.0f / (float)p->tile_m; /* exact for powers of two */
+    int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * p->tile_m);
+    oracle_tile_rows(p, Q, K, b, h, t, rows);
+    for (int k = 0; k < p->d; ++k) {
+        float sum = 0.0f;
+        for (int r = 0; r < p->tile_m; ++r) sum = sum + widen(Q, p->dtype, q_index(p, b, h, rows[r], k));
         qbar[k] = sum * inv;
     }
+    free(rows);
 }
 
 /* Representative query of the list tile t uses: the tile's mean, or (segment
  * lists) the mean of the segment's tile means: fp32 sum over the segment's
  * tiles in ascending order, then one multiplication by fl(1/number of tiles). */
-void oracle_rep_query(const oracle_problem *p, const void *Q, int b, int h, int t, float *qbar) {
+void oracle_rep_query(const oracle_problem *p, const void *Q, const void *K, int b, int h, int t, float *qbar) {
     if (!p->per_segment) {
-        oracle_pool(p, Q, b, h, t, qbar);
+        oracle_pool(p, Q, K, b, h, t, qbar);
         return;
     }
     int P = p->seg_len / p->tile_m;
@@ -187,7 +268,7 @@ void oracle_rep_query(const oracle_problem *p, const void *Q, int b, int h, int 
     float *tq = (float *)malloc(sizeof(float) * p->d);
     for (int k = 0; k < p->d; ++k) qbar[k] = 0.0f;
     for (int u = first; u < last; ++u) {
-        oracle_pool(p, Q, b, h, u, tq);
+        oracle_pool(p, Q, K, b, h, u, tq);
         for (int k = 0; k < p->d; ++k) qbar[k] = qbar[k] + tq[k];
     }
     float inv = 1.0f / (float)(last - first);
@@ -216,7 +297,7 @@ void oracle_score_tile(const oracle_problem *p, const void *Q, const void *K, in
     int64_t n = oracle_list_len(p, t);
     float *qbar = (float *)malloc(sizeof(float) * p->d);
     float *kbar = (float *)malloc(sizeof(float) * p->d);
-    oracle_rep_query(p, Q, b, h, t, qbar);
+    oracle_rep_query(p, Q, K, b, h, t, qbar);
     for (int64_t j = 0; j < n; ++j) {
         if (p->block_lists)
             oracle_pool_block(p, K, b, g, j, kbar);
@@ -309,9 +390,13 @@ int32_t oracle_attn_tile(const oracle_problem *p, const void *Q, const void *K, 
                          double *out, int32_t *n_exec, double *gstar) {
     int BM = p->tile_m, BN = p->tile_n, d = p->d;
     int g = h / (p->Hq / p->Hkv);
-    int64_t row0 = (int64_t)t * BM;
     int64_t a = oracle_seg_start(p, t);
     int32_t chunks = (int32_t)(a / BN);
+    int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * BM);
+    oracle_tile_rows(p, Q, K, b, h, t, rows);
+    int64_t last = rows[0];
+    for (int r = 1; r < BM; ++r)
+        if (rows[r] > last) last = rows[r];
     row_state *st = (row_state *)malloc(sizeof(row_state) * BM);
     double *accs = (double *)calloc((size_t)BM * d, sizeof(double));
     double *x = (double *)malloc(sizeof(double) * BN);
@@ -322,12 +407,13 @@ int32_t oracle_attn_tile(const oracle_problem *p, const void *Q, const void *K, 
         st[r].acc = accs + (size_t)r * d;
     }
 
-    /* pass 1: contiguous key tiles of the current segment, causal mask */
-    int32_t p1 = oracle_pass1_tiles(p, t);
+    /* pass 1: contiguous key tiles of the current segment up to the tile's last
+     * row, each row under its own causal mask */
+    int32_t p1 = (int32_t)((last + 1 - a + BN - 1) / BN);
     for (int32_t c = 0; c < p1; ++c) {
         int64_t k0 = a + (int64_t)c * BN;
         for (int r = 0; r < BM; ++r) {
-            int64_t i = row0 + r;
+            int64_t i = rows[r];
             int n = 0;
             for (int e = 0; e < BN; ++e)
                 if (k0 + e <= i) keys[n++] = k0 + e;
@@ -343,7 +429,7 @@ int32_t oracle_attn_tile(const oracle_problem *p, const void *Q, const void *K, 
             keys[e] = p->block_lists ? (int64_t)list[c] * BN + e : list[(int64_t)c * BN + e];
         double worst = 0.0; /* max over rows of g_i */
         for (int r = 0; r < BM; ++r) {
-            double mass = absorb(p, Q, K, V, b, h, g, row0 + r, keys, BN, &st[r], x);
+            double mass = absorb(p, Q, K, V, b, h, g, rows[r], keys, BN, &st[r], x);
             double gain = mass / st[r].l;
             if (gain > worst) worst = gain;
         }
@@ -355,6 +441,7 @@ int32_t oracle_attn_tile(const oracle_problem *p, const void *Q, const void *K, 
     for (int r = 0; r < BM; ++r)
         for (int k = 0; k < d; ++k) out[(size_t)r * d + k] = st[r].acc[k] / st[r].l;
     *n_exec = p1 + executed;
+    free(rows);
     free(keys);
     free(x);
     free(accs);
@@ -416,6 +503,13 @@ void oracle_scores_all(const oracle_problem *p, const void *Q, const void *K, fl
         if (oracle_list_len(p, t) > 0)
             oracle_score_tile(p, Q, K, b, h, t, scores + oracle_list_offset(p, b, h, t));
     }
+    if (!p->qperm) return;
+    int32_t nseg = num_segments(p);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < (int64_t)p->B * p->Hq * nseg; ++u) {
+        int b = (int)(u / ((int64_t)p->Hq * nseg)), h = (int)((u / nseg) % p->Hq), s = (int)(u % nseg);
+        oracle_query_scores(p, Q, K, b, h, s, scores + oracle_query_list_offset(p, b, h, s));
+    }
 }
 
 /* every list from the scores */
@@ -428,6 +522,14 @@ void oracle_lists_all(const oracle_problem *p, const float *scores, int32_t *lis
         int t = list_owner(p, (int)(u % U));
         int64_t off = oracle_list_offset(p, b, h, t);
         oracle_order(scores + off, oracle_list_len(p, t), lists + off);
+    }
+    if (!p->qperm) return;
+    int32_t nseg = num_segments(p);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < (int64_t)p->B * p->Hq * nseg; ++u) {
+        int b = (int)(u / ((int64_t)p->Hq * nseg)), h = (int)((u / nseg) % p->Hq), s = (int)(u % nseg);
+        int64_t off = oracle_query_list_offset(p, b, h, s);
+        oracle_order(scores + off, seg_rows(p, s), lists + off);
     }
 }
 

@@ -18,8 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "s2o_oracle.c")
 
 MUTANTS = {
-    "pool drops the last row": ("for (int r = 0; r < p->tile_m; ++r)",
-                                "for (int r = 0; r < p->tile_m - 1; ++r)"),
+    "pool drops the last row": ("for (int r = 0; r < p->tile_m; ++r) sum = sum",
+                                "for (int r = 0; r < p->tile_m - 1; ++r) sum = sum"),
     "score reads the wrong KV head": (
         "int g = h / (p->Hq / p->Hkv);\n    int64_t n = oracle_list_len(p, t);",
         "int g = h % p->Hkv;\n    int64_t n = oracle_list_len(p, t);"),
@@ -50,6 +50,12 @@ MUTANTS = {
     "block mean drops a row": ("for (int r = 0; r < p->tile_n; ++r)", "for (int r = 1; r < p->tile_n; ++r)"),
     "block chunk ignores the list": ("keys[e] = p->block_lists ? (int64_t)list[c] * BN + e",
                                      "keys[e] = p->block_lists ? (int64_t)c * BN + e"),
+    "guide drops the last key row": ("for (int64_t j = 0; j < n; ++j) sum = sum", "for (int64_t j = 0; j < n - 1; ++j) sum = sum"),
+    "query order ignored by the tiles": ("for (int r = 0; r < p->tile_m; ++r) rows[r] = a + order[row0 - a + r];",
+                                         "for (int r = 0; r < p->tile_m; ++r) rows[r] = row0 + r;"),
+    "pass 1 stops at the tile's first row": ("        if (rows[r] > last) last = rows[r];", "        if (rows[r] < last) last = rows[r];"),
+    "query score with the wrong head": ("acc = fmaf(widen(Q, p->dtype, q_index(p, b, h, a + i, k)), guide[k], acc);",
+                                        "acc = fmaf(widen(Q, p->dtype, q_index(p, b, (h + 1) % p->Hq, a + i, k)), guide[k], acc);"),
     "block scored by its first key": ("            oracle_pool_block(p, K, b, g, j, kbar);",
                                       "            for (int k = 0; k < p->d; ++k) kbar[k] = widen(K, p->dtype, kv_index(p, b, g, j * p->tile_n, k));"),
 }

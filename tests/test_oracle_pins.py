@@ -629,3 +629,111 @@ def test_block_scores_exact_on_dyadic_inputs():
             block = K[0, 0, c * BN:(c + 1) * BN].astype(np.int64)
             want = sum(Fraction(int(qrow[k])) * Fraction(int(block[:, k].sum()), BN) for k in range(d))
             assert Fraction(float(got[c])) == want
+
+
+# ------------------------------------------------------------------- Q_perm ---
+# Inside each segment the query rows are ordered by their score against a shared
+# guide vector, and query tiles are formed from that order (gist.science
+# summary, "Classement par Segment", Q_perm).  Reading: the guide is the
+# segment's mean key; each row keeps its own causal window in pass 1.
+
+QP_GEOMS = [
+    # B, Hq, Hkv, N, d, S, BM, BN, dtype
+    (1, 1, 1, 256, 16, 64, 16, 8, "f32"),
+    (2, 4, 2, 192, 8, 64, 8, 4, "f32"),     # GQA, batch 2
+    (1, 2, 1, 200, 8, 48, 8, 8, "bf16"),    # ragged last segment
+    (1, 2, 2, 256, 32, 64, 64, 64, "bf16"), # tile = segment
+]
+
+
+@pytest.mark.parametrize("geom", QP_GEOMS)
+def test_qperm_tau_zero_equals_dense_attention(geom):
+    """Every row still sees exactly its causal prefix, whatever tile it lands in."""
+    B, Hq, Hkv, N, d, S, BM, BN, dt = geom
+    Q, K, V = random_inputs(B, Hq, Hkv, N, d, seed=151 + N, dtype=dt)
+    ref = sdpa_fp64(oracle.problem(B, Hq, Hkv, N, d, dt, S, BM, BN, 1 / np.sqrt(d)), Q, K, V)
+    for per_segment in (False, True):
+        p = oracle.problem(B, Hq, Hkv, N, d, dt, S, BM, BN, 1 / np.sqrt(d), per_segment=per_segment,
+                           qperm=True)
+        T = N // BM
+        r = oracle.attn_tiles(p, Q, K, V, tiles_of(p), 0.0)
+        out = np.empty((B, Hq, N, d))
+        for n, (b, h, t) in enumerate(tiles_of(p)):
+            out[b, h, r["rows"][n]] = r["out"][n]
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_qperm_rows_partition_each_segment_in_score_order():
+    """The tiles of a segment hold every row of it exactly once, in Python's
+    (score descending, row ascending) order of the query scores."""
+    B, Hq, Hkv, N, d, S, BM = 1, 2, 1, 200, 8, 48, 8
+    Q, K, _ = random_inputs(B, Hq, Hkv, N, d, seed=9, dtype="bf16")
+    p = oracle.problem(B, Hq, Hkv, N, d, "bf16", S, BM, 8, 0.25, qperm=True)
+    for h in range(Hq):
+        for s in range((N + S - 1) // S):
+            a, e = s * S, min(N, (s + 1) * S)
+            sc = oracle.query_scores(p, Q, K, 0, h, s)
+            want = a + np.array(sorted(range(e - a), key=lambda i: (-float(sc[i]), i)))
+            got = np.concatenate([oracle.tile_rows(p, Q, K, 0, h, t) for t in range(a // BM, e // BM)])
+            assert np.array_equal(got, want)
+
+
+def test_qperm_guide_and_scores_exact_on_dyadic_inputs():
+    """Small integer keys and queries with a power-of-two segment: the guide is the
+    exact mean key and every query score the exact dot product with it."""
+    N, d, S, BM, Hq = 128, 8, 64, 16, 2
+    rng = np.random.default_rng(10)
+    K = rng.integers(-8, 9, size=(1, 1, N, d)).astype(np.float32)
+    Q = rng.integers(-3, 4, size=(1, Hq, N, d)).astype(np.float32)
+    p = oracle.problem(1, Hq, 1, N, d, "f32", S, BM, 8, 1.0, qperm=True)
+    for s in range(N // S):
+        keys = K[0, 0, s * S:(s + 1) * S].astype(np.int64)
+        gd = [Fraction(int(keys[:, k].sum()), S) for k in range(d)]
+        assert [Fraction(float(x)) for x in oracle.guide(p, K, 0, 0, s)] == gd
+        for h in range(Hq):
+            sc = oracle.query_scores(p, Q, K, 0, h, s)
+            for i in range(0, S, 7):
+                want = sum(Fraction(int(Q[0, h, s * S + i, k])) * gd[k] for k in range(d))
+                assert Fraction(float(sc[i])) == want
+
+
+def test_qperm_with_tied_scores_is_the_identity():
+    """Keys whose first four dimensions cancel in pairs give a guide that is exactly zero
+    there; queries living only in those dimensions then all score exactly 0, so Q_perm
+    keeps the row order and reproduces the unpermuted lists, counts and outputs exactly
+    (while the attention itself, q . k over those dimensions, is not trivial)."""
+    B, Hq, Hkv, N, d, S, BM, BN = 1, 2, 1, 256, 8, 64, 16, 8
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    K[0, 0, 1::2, :4] = -K[0, 0, 0::2, :4]        # pairs cancel exactly in the running sum
+    Q = np.zeros((1, Hq, N, d), np.float32)
+    Q[..., :4] = rng.standard_normal((1, Hq, N, 4))
+    V = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    p0 = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, BN, 0.5)
+    p1 = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, BN, 0.5, qperm=True)
+    for s_ in range(N // S):
+        assert not np.any(oracle.guide(p1, K, 0, 0, s_)[:4])
+        for h in range(Hq):
+            assert not np.any(oracle.query_scores(p1, Q, K, 0, h, s_))
+    o0, n0, _, _ = run_all(p0, Q, K, V, 0.02)
+    o1, n1, _, _ = run_all(p1, Q, K, V, 0.02)
+    assert np.array_equal(o0, o1) and np.array_equal(n0, n1)
+    assert np.any(n0 != n0.max())                  # the stop rule did fire somewhere
+    s0, s1 = oracle.scores_all(p0, Q, K), oracle.scores_all(p1, Q, K)
+    assert np.array_equal(s0, s1[:len(s0)])
+
+
+def test_qperm_pass1_window_and_layout():
+    """Pass 1 of a permuted tile covers key tiles up to its last row; the query orders
+    follow every key list, one run of N rows per (b, h)."""
+    B, Hq, Hkv, N, d, S, BM, BN = 1, 1, 1, 128, 8, 64, 16, 8
+    Q, K, V = random_inputs(B, Hq, Hkv, N, d, seed=12)
+    p = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, BN, 0.3, qperm=True)
+    pk = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, BN, 0.3)
+    assert oracle.list_entries(p) == oracle.list_entries(pk) + N
+    assert oracle.query_list_offset(p, 0, 0, 1) == oracle.list_entries(pk) + S
+    r = oracle.attn_tiles(p, Q, K, V, tiles_of(p), 1.0)   # tau >= 1: exactly one pass-2 chunk
+    for n, (_, _, t) in enumerate(tiles_of(p)):
+        a = t * BM // S * S
+        p1 = (int(r["rows"][n].max()) + 1 - a + BN - 1) // BN
+        assert r["n_exec"][n] == p1 + (1 if a > 0 else 0)

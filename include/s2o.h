@@ -98,12 +98,30 @@ enum {
     S2O_LISTS_PER_SEGMENT_BLOCKS = 3
 };
 
+/* Flag to OR into list_granularity: query permutation ([GIST] Classement par
+ * Segment, Q_perm).  Inside each segment the query rows are ordered by their
+ * score against a shared guide vector, here the segment's mean key (fp32 sum
+ * of its key rows in ascending order, times fl(1/rows)); a row's score is the
+ * fp32 fma chain over k of Q[row, k] * guide[k]; rows are sorted by score
+ * descending, ties to the lower row.  Query tile t of a segment holds the rows
+ * at positions t*BM .. t*BM+BM-1 of that order (positions count from the
+ * segment start like rows); its representative query is the fp32 sum of those
+ * rows in that order times 1/BM.  In attention each row keeps its own causal
+ * window (pass 1 covers key tiles up to the tile's last row) and its output
+ * goes to its own row.  The order of segment s of (b, h) is stored after all
+ * key lists: at (total key-list entries) + (b*Hq + h)*N + s*S, as row numbers
+ * relative to the segment start; the matching scores sit at the same offsets.
+ * bf16 problems with seg_len <= 8192 only (else S2O_ERR_UNSUPPORTED). */
+enum { S2O_QUERY_PERMUTATION = 4 };
+
 /* Validates a problem (sizes, divisibility, supported tiles).  Returns S2O_OK,
  * S2O_ERR_INVALID_ARG or S2O_ERR_UNSUPPORTED.  Pure host function. */
 s2o_status s2o_check_problem(const s2o_problem *p);
 
 /* Total list entries over all lists (per tile: B*Hq*sum_t a_t; per segment:
- * B*Hq*sum_s s*S).  -1 if the problem is invalid.  Pure host function. */
+ * B*Hq*sum_s s*S; divided by tile_n for block lists; plus B*Hq*N query-order
+ * entries with S2O_QUERY_PERMUTATION).  -1 if the problem is invalid.  Pure
+ * host function. */
 int64_t s2o_list_entries(const s2o_problem *p);
 
 /* Offset of the list tile t of (b, h) uses, in the layout above; -1 if out of
@@ -160,7 +178,8 @@ s2o_status s2o_build_index(const s2o_problem *p, const float *scores, int32_t *i
  * rounded to bf16 for PV; l and delta use fp32 P), and on fp32 MFMA for fp32
  * problems.
  *   idx: device int32 lists from s2o_build_index (or any lists in the layout
- *        above whose entries are in [0, a_t)).
+ *        above whose entries are in [0, a_t), and with S2O_QUERY_PERMUTATION
+ *        query orders that are permutations of each segment's rows).
  *   tau: >= 0 and not NaN.
  * Errors: INVALID_ARG, UNSUPPORTED (causal = 0), HIP. */
 s2o_status s2o_attn_fwd(const s2o_problem *p, const void *Q, const void *K, const void *V,

@@ -85,28 +85,30 @@ def _raise(fn: str, st: int):
 
 
 LISTS = {"tile": 0, "segment": 1, "tile_blocks": 2, "segment_blocks": 3}
+QUERY_PERMUTATION = 4
 LISTS_PER_TILE, LISTS_PER_SEGMENT = LISTS["tile"], LISTS["segment"]
 
 
 def problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, seg_len, tile_m=128,
-            tile_n=64, scale=None, causal=True, lists="tile") -> Problem:
+            tile_n=64, scale=None, causal=True, lists="tile", qperm=False) -> Problem:
     """dtype: torch.float32 / torch.bfloat16 (or 0 / 1).
     lists: "tile" (one list per query tile), "segment" (one list per segment), or
-    "tile_blocks" / "segment_blocks" (the same with blocks of tile_n keys as entries)."""
+    "tile_blocks" / "segment_blocks" (the same with blocks of tile_n keys as entries).
+    qperm: order the query rows of every segment by their guide score (Q_perm)."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
-    gran = LISTS[lists]
+    gran = LISTS[lists] | (QUERY_PERMUTATION if qperm else 0)
     return Problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, 1 if causal else 0,
                    seg_len, tile_m, tile_n, float(scale), gran)
 
 
 def problem_for(q: torch.Tensor, k: torch.Tensor, seg_len: int, tile=(128, 64), scale=None,
-                causal=True, lists="tile") -> Problem:
+                causal=True, lists="tile", qperm=False) -> Problem:
     B, Hq, N, d = q.shape
     return problem(B, Hq, k.shape[1], N, d, q.dtype, seg_len, tile[0], tile[1], scale, causal,
-                   lists)
+                   lists, qperm)
 
 
 def _stream() -> ctypes.c_void_p:
@@ -216,9 +218,10 @@ def dense_attn_fwd(p: Problem, q, k, v, out=None) -> torch.Tensor:
     return out
 
 
-def s2o_attention(q, k, v, tau: float, seg_len: int, tile=(128, 64), scale=None, lists="tile"):
+def s2o_attention(q, k, v, tau: float, seg_len: int, tile=(128, 64), scale=None, lists="tile",
+                  qperm=False):
     """Whole path: score -> build_index -> attention.  Returns (O, exec_tiles)."""
-    p = problem_for(q, k, seg_len, tile, scale, lists=lists)
+    p = problem_for(q, k, seg_len, tile, scale, lists=lists, qperm=qperm)
     scores = s2o_score(p, q, k)
     idx = s2o_build_index(p, scores)
     return s2o_attn_fwd(p, q, k, v, idx, tau)

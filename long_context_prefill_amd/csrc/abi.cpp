@@ -30,8 +30,10 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     if (p->head_dim != 64 && p->head_dim != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_m != 64 && p->tile_m != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_n != s2o::kTileN) return S2O_ERR_UNSUPPORTED;
-    if (p->list_granularity < S2O_LISTS_PER_TILE || p->list_granularity > S2O_LISTS_PER_SEGMENT_BLOCKS)
-        return S2O_ERR_INVALID_ARG;
+    if (p->list_granularity < 0 || p->list_granularity > 7) return S2O_ERR_INVALID_ARG;
+    if ((p->list_granularity & S2O_QUERY_PERMUTATION) &&
+        (p->dtype != S2O_BF16 || p->seg_len > s2o::kQuerySortCap))
+        return S2O_ERR_UNSUPPORTED;
 
     g.B = p->batch;
     g.Hq = p->heads_q;
@@ -49,6 +51,7 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     g.scale = p->scale;
     g.per_seg = p->list_granularity & 1;
     g.blocks = (p->list_granularity >> 1) & 1;
+    g.qperm = (p->list_granularity >> 2) & 1;
     g.nseg = (g.N + g.S - 1) / g.S;
     g.inv_P = 1.0f / (float)g.P;
     g.inv_P_last = 1.0f / (float)(g.T - (g.nseg - 1) * g.P);
@@ -63,6 +66,7 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     if (g.blocks) L /= g.BN;  // every history is a multiple of S, and S of BN
     g.list_per_head = L;
     g.list_entries = L * g.B * g.Hq;
+    g.query_entries = g.qperm ? (int64_t)g.B * g.Hq * g.N : 0;
     // index ranges the kernels assume
     const int64_t units = (int64_t)g.B * g.Hkv * g.T;
     if ((int64_t)g.B * g.Hq * g.T >= (1ll << 31) || ((units + 7) / 8) * 8 * g.G >= (1ll << 31))
@@ -97,7 +101,7 @@ s2o_status s2o_check_problem(const s2o_problem *p) {
 int64_t s2o_list_entries(const s2o_problem *p) {
     Geometry g;
     if (make_geometry(p, g) != S2O_OK) return -1;
-    return g.list_entries;
+    return g.list_entries + g.query_entries;
 }
 
 int64_t s2o_list_offset(const s2o_problem *p, int32_t b, int32_t h, int32_t t) {
@@ -113,13 +117,22 @@ size_t tile_query_bytes(const Geometry &g) { return ((size_t)g.B * g.Hq * g.T * 
 size_t segment_query_bytes(const Geometry &g) {
     return g.per_seg ? (((size_t)g.B * g.Hq * g.nseg * g.d * sizeof(float) + 255) & ~(size_t)255) : 0;
 }
+size_t block_key_bytes(const Geometry &g) {
+    return g.blocks ? (((size_t)g.B * g.Hkv * (g.N / g.BN) * g.d * sizeof(float) + 255) & ~(size_t)255) : 0;
+}
+size_t guide_bytes(const Geometry &g) {
+    return g.qperm ? (((size_t)g.B * g.Hkv * g.nseg * g.d * sizeof(float) + 255) & ~(size_t)255) : 0;
+}
+size_t query_order_bytes(const Geometry &g) {
+    return g.qperm ? (((size_t)g.query_entries * sizeof(int32_t) + 255) & ~(size_t)255) : 0;
+}
 }
 
 size_t s2o_score_workspace_bytes(const s2o_problem *p) {
     Geometry g;
     if (make_geometry(p, g) != S2O_OK) return 0;
-    const size_t blocks = g.blocks ? (size_t)g.B * g.Hkv * (g.N / g.BN) * g.d * sizeof(float) : 0;
-    return tile_query_bytes(g) + segment_query_bytes(g) + blocks;
+    return tile_query_bytes(g) + segment_query_bytes(g) + block_key_bytes(g) + guide_bytes(g) +
+           query_order_bytes(g);
 }
 
 s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *scores,
@@ -129,18 +142,29 @@ s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *
     if (st != S2O_OK) return st;
     if (!g.causal) return S2O_ERR_UNSUPPORTED;
     if (!Q || !K || !aligned16(Q) || !aligned16(K)) return S2O_ERR_INVALID_ARG;
-    if (g.list_entries > 0 && !scores) return S2O_ERR_INVALID_ARG;
+    if (g.list_entries + g.query_entries > 0 && (!scores || !aligned16(scores))) return S2O_ERR_INVALID_ARG;
     if (!workspace_ok(workspace, workspace_bytes, s2o_score_workspace_bytes(p))) return S2O_ERR_WORKSPACE;
-    if (g.list_entries == 0) return S2O_OK;
+    if (g.list_entries + g.query_entries == 0) return S2O_OK;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char *ws = reinterpret_cast<char *>(workspace);
     float *qbar = reinterpret_cast<float *>(ws);
     float *qseg = g.per_seg ? reinterpret_cast<float *>(ws + tile_query_bytes(g)) : nullptr;
-    hipError_t e = s2o::launch_pool(g, Q, qbar, qseg, s);
+    char *after = ws + tile_query_bytes(g) + segment_query_bytes(g);
+    float *kbar = reinterpret_cast<float *>(after);
+    float *guides = reinterpret_cast<float *>(after + block_key_bytes(g));
+    int32_t *qorder = reinterpret_cast<int32_t *>(after + block_key_bytes(g) + guide_bytes(g));
+    hipError_t e;
+    if (g.qperm) {  // Q_perm: query scores (after the key lists) and the query order
+        e = s2o::launch_query_scores(g, Q, K, guides, scores + g.list_entries, s);
+        if (e != hipSuccess) return S2O_ERR_HIP;
+        e = s2o::launch_query_sort(g, scores + g.list_entries, qorder, s);
+        if (e != hipSuccess) return S2O_ERR_HIP;
+    }
+    if (g.list_entries == 0) return S2O_OK;
+    e = s2o::launch_pool(g, Q, g.qperm ? qorder : nullptr, qbar, qseg, s);
     if (e != hipSuccess) return S2O_ERR_HIP;
     if (!g.blocks) return launch_status(s2o::launch_score(g, g.per_seg ? qseg : qbar, K, scores, s));
     // block lists: score the blocks' mean keys as the keys of the block geometry
-    float *kbar = reinterpret_cast<float *>(ws + tile_query_bytes(g) + segment_query_bytes(g));
     e = s2o::launch_pool_blocks(g, K, kbar, s);
     if (e != hipSuccess) return S2O_ERR_HIP;
     return launch_status(s2o::launch_score(s2o::block_geometry(g), g.per_seg ? qseg : qbar, kbar, scores, s));
@@ -158,12 +182,18 @@ s2o_status s2o_build_index(const s2o_problem *p, const float *scores, int32_t *i
     s2o_status st = make_geometry(p, g);
     if (st != S2O_OK) return st;
     if (!g.causal) return S2O_ERR_UNSUPPORTED;
-    if (g.list_entries > 0 && (!scores || !idx || !aligned16(scores) || !aligned16(idx)))
+    if (g.list_entries + g.query_entries > 0 && (!scores || !idx || !aligned16(scores) || !aligned16(idx)))
         return S2O_ERR_INVALID_ARG;
     const Geometry lg = list_geometry(g);
     if (!workspace_ok(workspace, workspace_bytes, s2o::sort_workspace_bytes(lg))) return S2O_ERR_WORKSPACE;
-    if (g.list_entries == 0) return S2O_OK;
-    return launch_status(s2o::launch_sort(lg, scores, idx, workspace, reinterpret_cast<hipStream_t>(stream)));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (g.list_entries > 0) {
+        hipError_t e = s2o::launch_sort(lg, scores, idx, workspace, s);
+        if (e != hipSuccess) return S2O_ERR_HIP;
+    }
+    if (g.qperm)  // the query order, after the key lists
+        return launch_status(s2o::launch_query_sort(g, scores + g.list_entries, idx + g.list_entries, s));
+    return S2O_OK;
 }
 
 s2o_status s2o_attn_fwd(const s2o_problem *p, const void *Q, const void *K, const void *V,
@@ -174,10 +204,10 @@ s2o_status s2o_attn_fwd(const s2o_problem *p, const void *Q, const void *K, cons
     if (!g.causal) return S2O_ERR_UNSUPPORTED;
     if (!Q || !K || !V || !O || !aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
         return S2O_ERR_INVALID_ARG;
-    if (g.list_entries > 0 && !idx) return S2O_ERR_INVALID_ARG;
+    if (g.list_entries + g.query_entries > 0 && !idx) return S2O_ERR_INVALID_ARG;
     if (isnan(tau) || tau < 0.0f) return S2O_ERR_INVALID_ARG;
-    return launch_status(s2o::launch_attention(g, Q, K, V, idx, tau, O, exec_tiles, true,
-                                               reinterpret_cast<hipStream_t>(stream)));
+    return launch_status(s2o::launch_attention(g, Q, K, V, idx, g.qperm ? idx + g.list_entries : nullptr, tau, O,
+                                               exec_tiles, true, reinterpret_cast<hipStream_t>(stream)));
 }
 
 s2o_status dense_attn_fwd(const s2o_problem *p, const void *Q, const void *K, const void *V,
@@ -192,7 +222,7 @@ s2o_status dense_attn_fwd(const s2o_problem *p, const void *Q, const void *K, co
     if (st != S2O_OK) return st;
     if (!Q || !K || !V || !O || !aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
         return S2O_ERR_INVALID_ARG;
-    return launch_status(s2o::launch_attention(g, Q, K, V, nullptr, 0.0f, O, nullptr, false,
+    return launch_status(s2o::launch_attention(g, Q, K, V, nullptr, nullptr, 0.0f, O, nullptr, false,
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -46,6 +46,7 @@ struct AttnParams {
     const void *v;
     void *o;
     const int32_t *idx;
+    const int32_t *qorder;  // Q_perm: row order of every segment (null: rows in place)
     int32_t *exec;
     Geometry g;
     float scale_log2;  // softmax scale * log2(e)
@@ -569,6 +570,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     unsigned char *lds = smem_raw;
     __shared__ int flags[2][NW];
+    __shared__ int row_max[NW];
 
     const Geometry &g = a.g;
     Work wk;
@@ -577,11 +579,31 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, half = lane >> 5;
     const int row0 = t * BM;
-    const int my_row = row0 + 32 * wave + li;
-
     const int seg_a = S2O ? (int)seg_start(g, t) : 0;
     const int base1 = seg_a;
-    const int n1 = g.causal ? (row0 + BM - base1) / BN : g.N / BN;
+
+    // Rows of this lane and the causal extent of the tile.  In place: the rows
+    // row0 + 32*wave + li.  With Q_perm the tile holds the rows at positions
+    // row0 .. row0+BM-1 of its segment's order; pass 1 then runs to the tile's
+    // last row and the diagonal mask applies from the wave's first row.
+    int my_row = row0 + 32 * wave + li;
+    int wave_first = row0 + 32 * wave, tile_last = row0 + BM - 1;
+    if (S2O && a.qorder) {
+        my_row = seg_a + a.qorder[((int64_t)b * g.Hq + h) * g.N + row0 + 32 * wave + li];
+        int lo = my_row, hi = my_row;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) {
+            lo = min(lo, __shfl_xor(lo, o));
+            hi = max(hi, __shfl_xor(hi, o));
+        }
+        wave_first = lo;
+        if (lane == 0) row_max[wave] = hi;
+        __syncthreads();
+        tile_last = row_max[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) tile_last = max(tile_last, row_max[w]);
+    }
+    const int n1 = g.causal ? (tile_last + 1 - base1 + BN - 1) / BN : g.N / BN;
     const int n2 = S2O ? seg_a / BN : 0;
     const int total = n1 + n2;
     const int32_t *list = S2O ? a.idx + list_offset(g, b, h, t) : nullptr;
@@ -730,7 +752,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
 
         const bool is_p2 = S2O && k >= n1;
         const int key0 = is_p2 ? 0 : base1 + k * BN;
-        if (!is_p2 && g.causal && key0 + BN - 1 > row0 + 32 * wave) mask_chunk(s0, s1, key0, my_row, half);
+        if (!is_p2 && g.causal && key0 + BN - 1 > wave_first) mask_chunk(s0, s1, key0, my_row, half);
         const float mx = pair_max(fmaxf(max16(s0), max16(s1))) * c;
         const float m_new = mx > m + kMaxSlack ? mx : m;
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
@@ -855,14 +877,15 @@ hipError_t launch_d(const AttnParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attention(const Geometry &g, const void *Q, const void *K, const void *V,
-                            const int32_t *idx, float tau, void *O, int32_t *exec_tiles,
-                            bool s2o, hipStream_t stream) {
+                            const int32_t *idx, const int32_t *qorder, float tau, void *O,
+                            int32_t *exec_tiles, bool s2o, hipStream_t stream) {
     AttnParams p;
     p.q = Q;
     p.k = K;
     p.v = V;
     p.o = O;
     p.idx = idx;
+    p.qorder = qorder;
     p.exec = exec_tiles;
     p.g = g;
     p.scale_log2 = g.scale * 1.4426950408889634f;

@@ -18,10 +18,12 @@ struct Geometry {
     int32_t dtype;           // 0 fp32, 1 bf16
     int32_t per_seg;         // lists per segment (1) or per query tile (0)
     int32_t blocks;          // list entries are blocks of BN keys (1) or keys (0)
+    int32_t qperm;           // query rows ordered within segments (Q_perm)
     int32_t nseg;            // segments, the last one possibly partial
     float inv_P, inv_P_last; // fl(1/tiles) of a full and of the last segment
     int64_t list_per_head;   // L: list entries of one (b, h)
-    int64_t list_entries;    // B * Hq * L
+    int64_t list_entries;    // B * Hq * L (key lists)
+    int64_t query_entries;   // B * Hq * N with Q_perm (the query orders, after the key lists), else 0
     float scale;
 };
 
@@ -62,10 +64,16 @@ inline Geometry block_geometry(const Geometry &g) {
 
 // Kernel launchers (return hipSuccess or the launch error).
 hipError_t launch_attention(const Geometry &g, const void *Q, const void *K, const void *V,
-                            const int32_t *idx, float tau, void *O, int32_t *exec_tiles,
-                            bool s2o, hipStream_t stream);
+                            const int32_t *idx, const int32_t *qorder, float tau, void *O,
+                            int32_t *exec_tiles, bool s2o, hipStream_t stream);
 
-hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, float *qseg, hipStream_t stream);
+hipError_t launch_pool(const Geometry &g, const void *Q, const int32_t *qorder, float *qbar, float *qseg,
+                       hipStream_t stream);
+// Q_perm: segment guides (mean keys), query scores, and the per-segment query order
+hipError_t launch_query_scores(const Geometry &g, const void *Q, const void *K, float *guides, float *qscores,
+                               hipStream_t stream);
+hipError_t launch_query_sort(const Geometry &g, const float *qscores, int32_t *qorder, hipStream_t stream);
+constexpr int kQuerySortCap = 8192;  // longest segment the query sort holds in LDS
 hipError_t launch_pool_blocks(const Geometry &g, const void *K, float *kbar, hipStream_t stream);
 hipError_t launch_score(const Geometry &g, const float *qrep, const void *K, float *scores,
                         hipStream_t stream);

@@ -33,18 +33,26 @@ __device__ inline float widen<__bf16>(__bf16 x) {
     return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, x) << 16);
 }
 
+// qorder (Q_perm, else null): the rows of tile t are seg_start + qorder[bh*N +
+// t*BM + r], r = 0..BM-1, summed in that order.
 template <typename T>
-__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, float *__restrict__ qbar,
-                                                   Geometry g, int64_t total) {
+__global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, const int32_t *__restrict__ qorder,
+                                                   float *__restrict__ qbar, Geometry g, int64_t total) {
     int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= total) return;
     const int k = (int)(gid % g.d);
     const int64_t tile = gid / g.d;  // (b*Hq + h)*T + t
     const int t = (int)(tile % g.T);
     const int64_t bh = tile / g.T;
-    const T *src = Q + (bh * g.N + (int64_t)t * g.BM) * g.d + k;
+    const T *src = Q + bh * g.N * g.d + k;
+    const int64_t row0 = (int64_t)t * g.BM, a = seg_start(g, t);
     float sum = 0.0f;
-    for (int r = 0; r < g.BM; ++r) sum = sum + widen<T>(src[(int64_t)r * g.d]);
+    if (qorder) {
+        const int32_t *ord = qorder + bh * g.N + row0;
+        for (int r = 0; r < g.BM; ++r) sum = sum + widen<T>(src[(a + ord[r]) * g.d]);
+    } else {
+        for (int r = 0; r < g.BM; ++r) sum = sum + widen<T>(src[(row0 + r) * g.d]);
+    }
     // stored lane-major: element k of a pooled query at (k % 16) * (d / 16) + k / 16,
     // so a lane reads its d/16 elements (16c + lane, c = 0..) as one contiguous run
     qbar[tile * g.d + (k & 15) * (g.d >> 4) + (k >> 4)] = sum * (1.0f / (float)g.BM);  // exact: BM = 2^n
@@ -83,6 +91,95 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T *__restrict__ 
     float sum = 0.0f;
     for (int r = 0; r < g.BN; ++r) sum = sum + widen<T>(src[(int64_t)r * g.d]);
     kbar[gid] = sum * (1.0f / (float)g.BN);
+}
+
+// ---- Q_perm ----------------------------------------------------------------
+// Guide of segment s for KV head kvh: the segment's mean key, fp32 sum of its
+// rows in ascending order times fl(1/rows).  One thread per (b, kvh, s, k).
+template <typename T>
+__global__ __launch_bounds__(256) void guide_kernel(const T *__restrict__ K, float *__restrict__ guides,
+                                                    Geometry g, int64_t total) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int k = (int)(gid % g.d);
+    const int64_t unit = gid / g.d;  // (b*Hkv + kvh)*nseg + s
+    const int s = (int)(unit % g.nseg);
+    const int64_t bg = unit / g.nseg;
+    const int64_t a = (int64_t)s * g.S;
+    const int64_t n = ((a + g.S) < g.N ? (a + g.S) : (int64_t)g.N) - a;
+    const T *src = K + (bg * g.N + a) * g.d + k;
+    float sum = 0.0f;
+    for (int64_t j = 0; j < n; ++j) sum = sum + widen<T>(src[j * g.d]);
+    guides[gid] = sum * (1.0f / (float)n);
+}
+
+// Importance score of every query row: fma chain over k of Q[row, k] times the
+// guide of its segment, ascending k.  One thread per (b, h, row); written at
+// the row's own position of the query-order region.
+template <typename T>
+__global__ __launch_bounds__(256) void query_score_kernel(const T *__restrict__ Q, const float *__restrict__ guides,
+                                                          float *__restrict__ qscores, Geometry g, int64_t total) {
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int64_t bh = gid / g.N;
+    const int row = (int)(gid % g.N);
+    const int b = (int)(bh / g.Hq), h = (int)(bh % g.Hq);
+    const float *gd = guides + (((int64_t)b * g.Hkv + h / g.G) * g.nseg + row / g.S) * g.d;
+    const T *q = Q + gid * g.d;
+    float acc = 0.0f;
+    for (int k = 0; k < g.d; ++k) acc = __builtin_fmaf(widen<T>(q[k]), gd[k], acc);
+    qscores[gid] = acc;
+}
+
+// Query order of one segment of one (b, h): its rows sorted by score
+// descending, ties to the lower row.  One workgroup sorts the segment in LDS
+// with a bitonic network on (order-preserving key, row): the pair is unique, so
+// the network's instability does not matter.  The segment is padded to a power
+// of two with entries that sort after every real one.
+constexpr int QSORT_THREADS = 1024;
+__device__ inline uint32_t score_key(float f) {  // ascending key = descending score; -0 == +0
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0) u = 0;
+    const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ~asc;
+}
+__global__ __launch_bounds__(QSORT_THREADS) void query_sort_kernel(const float *__restrict__ qscores,
+                                                                   int32_t *__restrict__ qorder, Geometry g) {
+    __shared__ uint32_t key[kQuerySortCap];
+    __shared__ int32_t row[kQuerySortCap];
+    const int s = blockIdx.x % g.nseg;
+    const int64_t bh = blockIdx.x / g.nseg;
+    const int64_t a = (int64_t)s * g.S;
+    const int n = (int)(((a + g.S) < g.N ? (a + g.S) : (int64_t)g.N) - a);
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    const float *src = qscores + bh * g.N + a;
+    for (int i = threadIdx.x; i < n2; i += QSORT_THREADS) {
+        key[i] = i < n ? score_key(src[i]) : 0xFFFFFFFFu;  // real keys stay below 0xFF800000
+        row[i] = i;
+    }
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n2; i += QSORT_THREADS) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const uint32_t ki = key[i], kl = key[l];
+                    const int32_t ri = row[i], rl = row[l];
+                    const bool gt = ki > kl || (ki == kl && ri > rl);
+                    if (gt == ((i & k) == 0)) {  // ascending where bit k of i is clear
+                        key[i] = kl;
+                        key[l] = ki;
+                        row[i] = rl;
+                        row[l] = ri;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    int32_t *dst = qorder + bh * g.N + a;
+    for (int i = threadIdx.x; i < n; i += QSORT_THREADS) dst[i] = row[i];
 }
 
 constexpr int SCORE_KEYS = 256;   // keys per workgroup (one per thread)
@@ -233,20 +330,45 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
 
 }  // namespace
 
-hipError_t launch_pool(const Geometry &g, const void *Q, float *qbar, float *qseg, hipStream_t stream) {
+hipError_t launch_pool(const Geometry &g, const void *Q, const int32_t *qorder, float *qbar, float *qseg,
+                       hipStream_t stream) {
     int64_t total = (int64_t)g.B * g.Hq * g.T * g.d;
     unsigned blocks = (unsigned)((total + 255) / 256);
     if (g.dtype == 1)
         hipLaunchKernelGGL(pool_kernel<__bf16>, dim3(blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const __bf16 *>(Q), qbar, g, total);
+                           reinterpret_cast<const __bf16 *>(Q), qorder, qbar, g, total);
     else
         hipLaunchKernelGGL(pool_kernel<float>, dim3(blocks), dim3(256), 0, stream,
-                           reinterpret_cast<const float *>(Q), qbar, g, total);
+                           reinterpret_cast<const float *>(Q), qorder, qbar, g, total);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !g.per_seg) return e;
     int64_t stotal = (int64_t)g.B * g.Hq * g.nseg * g.d;
     hipLaunchKernelGGL(segpool_kernel, dim3((unsigned)((stotal + 255) / 256)), dim3(256), 0, stream,
                        qbar, qseg, g, stotal);
+    return hipGetLastError();
+}
+
+hipError_t launch_query_scores(const Geometry &g, const void *Q, const void *K, float *guides, float *qscores,
+                               hipStream_t stream) {
+    const int64_t gtotal = (int64_t)g.B * g.Hkv * g.nseg * g.d;
+    const int64_t qtotal = (int64_t)g.B * g.Hq * g.N;
+    if (g.dtype == 1) {
+        hipLaunchKernelGGL(guide_kernel<__bf16>, dim3((unsigned)((gtotal + 255) / 256)), dim3(256), 0, stream,
+                           reinterpret_cast<const __bf16 *>(K), guides, g, gtotal);
+        hipLaunchKernelGGL(query_score_kernel<__bf16>, dim3((unsigned)((qtotal + 255) / 256)), dim3(256), 0,
+                           stream, reinterpret_cast<const __bf16 *>(Q), guides, qscores, g, qtotal);
+    } else {
+        hipLaunchKernelGGL(guide_kernel<float>, dim3((unsigned)((gtotal + 255) / 256)), dim3(256), 0, stream,
+                           reinterpret_cast<const float *>(K), guides, g, gtotal);
+        hipLaunchKernelGGL(query_score_kernel<float>, dim3((unsigned)((qtotal + 255) / 256)), dim3(256), 0,
+                           stream, reinterpret_cast<const float *>(Q), guides, qscores, g, qtotal);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_query_sort(const Geometry &g, const float *qscores, int32_t *qorder, hipStream_t stream) {
+    hipLaunchKernelGGL(query_sort_kernel, dim3((unsigned)((int64_t)g.B * g.Hq * g.nseg)), dim3(QSORT_THREADS), 0,
+                       stream, qscores, qorder, g);
     return hipGetLastError();
 }
 

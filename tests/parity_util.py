@@ -40,21 +40,21 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def gpu_problem(w, seg_len=None, lists="tile"):
+def gpu_problem(w, seg_len=None, lists="tile", qperm=False):
     return s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0,
                        w.seg_len if seg_len is None else seg_len, w.tile_m, w.tile_n, w.scale,
-                       lists=lists)
+                       lists=lists, qperm=qperm)
 
 
 class GpuRun:
     """Inputs on the device plus scores and lists from the HIP path."""
 
-    def __init__(self, w, x, seg_len=None, lists="tile"):
+    def __init__(self, w, x, seg_len=None, lists="tile", qperm=False):
         self.w = w
         self.lists = lists
-        self.p = gpu_problem(w, seg_len, lists)
+        self.p = gpu_problem(w, seg_len, lists, qperm)
         self.po = oracle.problem_from_workload(w, seg_len, per_segment=lists.startswith("segment"),
-                                               block_lists=lists.endswith("blocks"))
+                                               block_lists=lists.endswith("blocks"), qperm=qperm)
         self.x = x
         self.q, self.k, self.v = (to_device(x[n]) for n in ("q", "k", "v"))
         say(f"{w.name}: score + build_index ({lists} lists, {s2o.list_entries(self.p)} entries)")
@@ -117,7 +117,7 @@ def compare(run: GpuRun, tiles, tau, o_gpu, ex_gpu, check_lists=True):
                 rep["list_mismatch"] += 1
         ng, no = int(ex[b, h, t]), int(res["n_exec"][n])
         if ng != no:
-            p1 = oracle.pass1_tiles(po, t)
+            p1 = int(res["n_exec"][n]) - int(res["chunks"][n])
             c = min(ng, no) - p1 - 1
             g = res["gstar"][n, c] if c >= 0 else -1.0
             if c >= 0 and abs(g - tau) <= NEAR_TAU_REL * tau:
@@ -127,7 +127,8 @@ def compare(run: GpuRun, tiles, tau, o_gpu, ex_gpu, check_lists=True):
                 rep["exec_mismatch"] += 1
                 say(f"exec mismatch at {(b, h, t)}: gpu {ng} oracle {no} (gain {g}, tau {tau})")
             continue
-        og = f64(o_gpu[b, h, t * BM:(t + 1) * BM])
+        rows = res["rows"][n] if res["rows"] is not None else np.arange(t * BM, (t + 1) * BM)
+        og = f64(o_gpu[b, h][torch.as_tensor(rows, device=o_gpu.device)])
         d = np.abs(og - res["out"][n])
         rep["max_abs"] = max(rep["max_abs"], float(d.max()))
         rep["sum_abs"] += float(d.sum())
@@ -136,7 +137,8 @@ def compare(run: GpuRun, tiles, tau, o_gpu, ex_gpu, check_lists=True):
         fres = oracle.attn_tiles(po, run.x["q"], run.x["k"], run.x["v"], [f[1] for f in forced],
                                  tau, force_n=[f[2] for f in forced])
         for i, (_, (b, h, t), _) in enumerate(forced):
-            og = f64(o_gpu[b, h, t * BM:(t + 1) * BM])
+            rows = fres["rows"][i] if fres["rows"] is not None else np.arange(t * BM, (t + 1) * BM)
+            og = f64(o_gpu[b, h][torch.as_tensor(rows, device=o_gpu.device)])
             d = np.abs(og - fres["out"][i])
             rep["max_abs"] = max(rep["max_abs"], float(d.max()))
             rep["sum_abs"] += float(d.sum())

@@ -110,7 +110,7 @@ def test_workspace_sizes():
     ("batch", 0, INVALID), ("heads_q", 3, INVALID), ("seq_len", 1000, INVALID),
     ("seg_len", 200, INVALID), ("head_dim", 96, UNSUPPORTED), ("tile_m", 256, UNSUPPORTED),
     ("tile_n", 32, UNSUPPORTED), ("dtype", 7, INVALID), ("causal", 2, INVALID),
-    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 4, INVALID), ("list_granularity", -1, INVALID)])
+    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 8, INVALID), ("list_granularity", -1, INVALID)])
 def test_problem_validation(field, value, code):
     p = base_problem()
     setattr(p, field, value)
@@ -176,3 +176,21 @@ def test_python_binding_raises_without_device_tensors():
     q = torch.zeros(1, 4, 1024, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         s2o.dense_attn_fwd(p, q, q[:, :2].contiguous(), q[:, :2].contiguous())
+
+
+@pytest.mark.parametrize("lists", ["tile", "segment", "tile_blocks"])
+def test_query_permutation_layout_and_validation(lists):
+    """Q_perm appends one run of N query-order entries per (b, h) after every key list."""
+    N, S, BM, B, Hq = 2048, 512, 128, 2, 3
+    p = base_problem(batch=B, heads_q=Hq, heads_kv=1, seq_len=N, seg_len=S, tile_m=BM, lists=lists,
+                     qperm=True)
+    assert s2o.check_problem(p) == 0
+    po = oracle.problem(B, Hq, 1, N, 128, "bf16", S, BM, 64, 1.0, per_segment=lists.startswith("segment"),
+                        block_lists=lists.endswith("blocks"), qperm=True)
+    pk = base_problem(batch=B, heads_q=Hq, heads_kv=1, seq_len=N, seg_len=S, tile_m=BM, lists=lists)
+    assert s2o.list_entries(p) == oracle.list_entries(po) == s2o.list_entries(pk) + B * Hq * N
+    for b, h, t in [(0, 0, 5), (1, 2, 15)]:
+        assert s2o.list_offset(p, b, h, t) == s2o.list_offset(pk, b, h, t) == oracle.list_offset(po, b, h, t)
+    # fp32 inputs and segments beyond the in-LDS query sort are not compiled
+    assert s2o.check_problem(base_problem(dtype=0, qperm=True)) == UNSUPPORTED
+    assert s2o.check_problem(base_problem(seq_len=32768, seg_len=16384, qperm=True)) == UNSUPPORTED

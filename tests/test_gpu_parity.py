@@ -435,3 +435,56 @@ def test_llama8b_128k_block_lists_sampled():
     tiles = sample_tiles(w, heads=(5, 22), n_random=8, seed=8)
     o, ex = run.attn(1e-3)
     assert_report(compare(run, tiles, 1e-3, o, ex, check_lists=True), "bf16")
+
+
+# ------------------------------------------------------------------- Q_perm ---
+# Query rows ordered within each segment by their score against the segment's
+# mean key; tiles are formed from that order (gist.science summary, "Classement
+# par Segment", Q_perm).
+
+QP_SMALL = [c for c in SMALL if c[0] in ("gqa_ragged_d128_bm128", "d64_bm64", "d128_bm64")]
+
+
+@pytest.mark.parametrize("lists", ["tile", "segment", "tile_blocks"])
+@pytest.mark.parametrize("case", QP_SMALL, ids=[c[0] for c in QP_SMALL])
+def test_small_bf16_query_permutation_every_tile(case, lists):
+    name, B, Hq, Hkv, N, d, BM, S, structure = case
+    w = synth.custom_workload(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", tile_m=BM, tile_n=64,
+                              seg_len=S, structure=structure, n_stripes=max(N // 100, 4),
+                              seed=1100 + N + d, name=name)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists=lists, qperm=True)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    for tau in (0.0, 1e-3, 3e-2):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, all_tiles(w), tau, o, ex, check_lists=False), "bf16")
+
+
+def test_llama8b_16k_query_permutation():
+    w = synth.WORKLOADS["llama8b_n16k"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="tile", qperm=True)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    tiles = sample_tiles(w, heads=(0, 9, 18, 27), n_random=16, seed=9)
+    for tau in (1e-2, 1e-3):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex, check_lists=False), "bf16")
+    o, ex = run.attn(0.0)
+    od = run.dense()
+    d = (o.float() - od.float()).abs()
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_128k_query_permutation_sampled():
+    w = synth.WORKLOADS["llama8b_n128k"]
+    say("generating llama8b_n128k inputs")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists="tile", qperm=True)
+    tiles = sample_tiles(w, heads=(7, 25), n_random=8, seed=10)
+    o, ex = run.attn(1.2e-3)
+    assert_report(compare(run, tiles, 1.2e-3, o, ex, check_lists=True), "bf16")

@@ -11,9 +11,10 @@ dense_attn_fwd over all B*Hq*N*d elements, fp32), unless --tau is given.
 
 The headline uses one index list per query tile.  The same measurement with
 one list per segment (shared by the segment's tiles) is reported under
-"segment_lists", and with blocks of 64 keys as list entries (the
+"segment_lists", with blocks of 64 keys as list entries (the
 block-granularity counterpart the method is compared with) under
-"block_lists".  "ranking_study" measures, on sampled tiles, how well each
+"block_lists", and with the query rows of every segment ordered by their
+guide score (Q_perm) under "query_permutation".  "ranking_study" measures, on sampled tiles, how well each
 list's order matches every row's true attention order.
 
 Prints one JSON line (rank 0, one GPU).  Extra fields: per-phase times, the
@@ -60,7 +61,7 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--tile-lists-only", action="store_true",
                     help="skip the per-segment-list measurement")
-    ap.add_argument("--modes", default="segment,tile_blocks",
+    ap.add_argument("--modes", default="segment,tile_blocks,tile+qperm",
                     help="list forms measured besides the headline per-tile lists")
     ap.add_argument("--no-ranking-study", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -84,7 +85,7 @@ def traffic_figure():
     return rec.get("hbm_bytes_per_launch")
 
 
-def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles):
+def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles, rows_of=None):
     """How well a tile's list order matches each row's true attention order.
 
     For every sampled tile (b, h, t) with history a > 0, E is the set of history
@@ -105,12 +106,16 @@ def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles):
         a = (t * w.tile_m // w.seg_len) * w.seg_len
         if a == 0:
             continue
-        n = int(exec_tiles[b, h, t]) - ((t + 1) * w.tile_m - a) // BN
+        p1 = ((t + 1) * w.tile_m - a) // BN
+        if rows_of:  # permuted rows: pass 1 runs to the tile's last row
+            p1 = (int(rows_of(b, h, t).max()) + 1 - a + BN - 1) // BN
+        n = int(exec_tiles[b, h, t]) - p1
         off = offsets(b, h, t)
         ent = idx[off:off + (a // BN if lists.endswith("blocks") else a)]
         order = (ent[:, None] * BN + np.arange(BN)).ravel() if lists.endswith("blocks") else ent
         widen = synth.f32_from_bf16_bits if w.dtype == "bf16" else (lambda z: np.asarray(z, np.float32))
-        q = widen(x["q"][b, h, t * w.tile_m:(t + 1) * w.tile_m])
+        rows = rows_of(b, h, t) if rows_of else np.arange(t * w.tile_m, (t + 1) * w.tile_m)
+        q = widen(x["q"][b, h, rows])
         k = widen(x["k"][b, h // G, :a])
         xl = (q @ k.T) * np.float32(w.scale)                       # [BM, a]
         ex = np.exp(xl - xl.max(axis=1, keepdims=True))
@@ -195,10 +200,12 @@ def main():
     log(f"dense_attn_fwd {dense_ms:.2f} ms ({dense_tiles * flop_per_tile / dense_ms / 1e9:.0f} TFLOP/s)")
     dsq = float((out_dense.float() ** 2).mean())
 
-    def run_mode(lists, steps, warmup, tau_fixed):
-        """tau sweep (untimed), then `steps` timed steps of score -> build_index -> attention."""
+    def run_mode(mode, steps, warmup, tau_fixed):
+        """tau sweep (untimed), then `steps` timed steps of score -> build_index -> attention.
+        mode: a list form ("tile", "segment", "tile_blocks", ...), "+qperm" for Q_perm."""
+        lists, qperm = mode.split("+")[0], mode.endswith("+qperm")
         p = s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0, w.seg_len,
-                        w.tile_m, w.tile_n, w.scale, lists=lists)
+                        w.tile_m, w.tile_n, w.scale, lists=lists, qperm=qperm)
         n_list = s2o.list_entries(p)
         scores = torch.empty(max(n_list, 1), dtype=torch.float32, device="cuda")
         idx = torch.empty(max(n_list, 1), dtype=torch.int32, device="cuda")
@@ -215,7 +222,7 @@ def main():
             mse = float(((out.float() - out_dense.float()) ** 2).mean())
             density = float(exec_tiles.sum()) / dense_tiles
             sweep.append({"tau": tau, "density": round(density, 4), "mse": mse, "rel_mse": mse / dsq})
-            log(f"[{lists} lists] tau {tau:g}: density {density:.4f} mse {mse:.3e}")
+            log(f"[{mode}] tau {tau:g}: density {density:.4f} mse {mse:.3e}")
         ok = [r for r in sweep if r["mse"] <= MSE_BUDGET]
         chosen = max(ok, key=lambda r: r["tau"]) if ok else min(sweep, key=lambda r: r["tau"])
         tau = chosen["tau"]
@@ -245,11 +252,17 @@ def main():
         achieved = executed * flop_per_tile / (attn_ms * 1e-3) / 1e12
         study = None
         if not args.no_ranking_study:
-            log(f"[{lists} lists] ranking study on {len(study_tiles)} tiles")
-            study = ranking_study(w, x, lists, idx.cpu().numpy(),
-                                  lambda b_, h_, t_: s2o.list_offset(p, b_, h_, t_),
-                                  exec_tiles.cpu().numpy(), study_tiles)
-        log(f"[{lists} lists] step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index "
+            log(f"[{mode}] ranking study on {len(study_tiles)} tiles")
+            idx_h = idx.cpu().numpy()
+            n_keys = s2o.list_entries(p) - (w.B * w.Hq * w.N if qperm else 0)
+
+            def rows_of(b_, h_, t_):  # Q_perm: the tile's rows from the stored query order
+                a_ = (t_ * w.tile_m // w.seg_len) * w.seg_len
+                o_ = n_keys + (b_ * w.Hq + h_) * w.N + t_ * w.tile_m
+                return a_ + idx_h[o_:o_ + w.tile_m].astype(np.int64)
+            study = ranking_study(w, x, lists, idx_h, lambda b_, h_, t_: s2o.list_offset(p, b_, h_, t_),
+                                  exec_tiles.cpu().numpy(), study_tiles, rows_of if qperm else None)
+        log(f"[{mode}] step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index "
             f"{sort_ms:.2f} + attn {attn_ms:.2f}")
         res = {"tau": tau, "ms_per_step": ms_per_step, "score_ms": score_ms, "sort_ms": sort_ms,
                "attn_ms": attn_ms, "executed": executed, "density": executed / dense_tiles,
@@ -303,7 +316,8 @@ def main():
                      "work": f"{main['executed']} executed 128x64 tiles x {flop_per_tile:.0f} flop"},
     }
     names = {"segment": "segment_lists", "tile_blocks": "block_lists",
-             "segment_blocks": "segment_block_lists"}
+             "segment_blocks": "segment_block_lists", "tile+qperm": "query_permutation",
+             "segment+qperm": "segment_lists_query_permutation"}
     for m, r in extra.items():
         rec[names.get(m, m + "_lists")] = {
             "ms_per_step": round(r["ms_per_step"], 3), "tau": r["tau"],

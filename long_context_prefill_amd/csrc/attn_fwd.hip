@@ -747,8 +747,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         constexpr int kst = decltype(kst_c)::value;
         if (k + 2 < total) issue_k(kst, krows);            // K_{k+2} -> stage of K_k
         if (k + 1 < total) issue_v(kst ^ 1, vrows);        // V_{k+1} -> stage of V_{k-1}
+        // V_{k+2} moves the rows K_{k+2} just used: keep them instead of reloading
+#pragma unroll
+        for (int i = 0; i < C::INSTR; ++i) vrows[i] = krows[i];
         if (k + 3 < total) fetch_rows(k + 3, krows);
-        if (k + 2 < total) fetch_rows(k + 2, vrows);
 
         const bool is_p2 = S2O && k >= n1;
         const int key0 = is_p2 ? 0 : base1 + k * BN;

@@ -7,7 +7,9 @@ are resident in HBM before timing starts.
 
 Before timing, tau is chosen as the largest value of a fixed sweep whose
 output stays within a dense-relative MSE of 1e-5 (MSE against this library's
-dense_attn_fwd over all B*Hq*N*d elements, fp32), unless --tau is given.
+dense_attn_fwd over all B*Hq*N*d elements, fp32), then refined by a few
+geometric bisection steps between it and the next sweep value (whose MSE is
+above the budget); --tau skips both.
 
 The headline uses one index list per query tile.  The same measurement with
 one list per segment (shared by the segment's tiles) is reported under
@@ -43,6 +45,33 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_s2o_attn_fwd_llama8b_n128k.json")
 ATTN_SOURCE = os.path.join(ROOT, "long_context_prefill_amd", "csrc", "attn_fwd.hip")
+
+
+def refine_tau(sweep, evaluate, budget=MSE_BUDGET, steps=4):
+    """Bisect (geometrically) between the largest sweep tau within `budget` and
+    the smallest one above it.  `evaluate(tau)` returns a sweep record with an
+    "mse" field; the records it makes are appended to `sweep` (marked
+    "refined") and the largest tau found within budget is returned, or None
+    when the sweep has no such bracket."""
+    ok = [r["tau"] for r in sweep if r["mse"] <= budget]
+    bad = [r["tau"] for r in sweep if r["mse"] > budget]
+    if not ok:
+        return None
+    lo = max(ok)
+    above = [t for t in bad if t > lo]
+    if not above or lo <= 0.0:
+        return lo
+    hi = min(above)
+    for _ in range(steps):
+        mid = float(np.sqrt(lo * hi))
+        r = evaluate(mid)
+        r["refined"] = True
+        sweep.append(r)
+        if r["mse"] <= budget:
+            lo = mid
+        else:
+            hi = mid
+    return lo
 
 
 def log(msg):
@@ -215,14 +244,17 @@ def main():
         exec_tiles = torch.empty((w.B, w.Hq, T), dtype=torch.int32, device="cuda")
         s2o.s2o_score(p, q, k, scores, ws_score)
         s2o.s2o_build_index(p, scores, idx, ws_sort)
-        sweep = []
-        taus = [tau_fixed] if tau_fixed is not None else sorted(w.taus, reverse=True)
-        for tau in taus:
+        def evaluate(tau):
             s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
             mse = float(((out.float() - out_dense.float()) ** 2).mean())
             density = float(exec_tiles.sum()) / dense_tiles
-            sweep.append({"tau": tau, "density": round(density, 4), "mse": mse, "rel_mse": mse / dsq})
             log(f"[{mode}] tau {tau:g}: density {density:.4f} mse {mse:.3e}")
+            return {"tau": tau, "density": round(density, 4), "mse": mse, "rel_mse": mse / dsq}
+
+        taus = [tau_fixed] if tau_fixed is not None else sorted(w.taus, reverse=True)
+        sweep = [evaluate(tau) for tau in taus]
+        if tau_fixed is None:
+            refine_tau(sweep, evaluate)
         ok = [r for r in sweep if r["mse"] <= MSE_BUDGET]
         chosen = max(ok, key=lambda r: r["tau"]) if ok else min(sweep, key=lambda r: r["tau"])
         tau = chosen["tau"]

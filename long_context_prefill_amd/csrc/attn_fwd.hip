@@ -760,10 +760,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         m = m_new;
 
+        // (before the matrix-core phase: its branch would otherwise split the
+        // exponentials from the products they are meant to overlap)
+        rescale(acc, alpha);
         // phase 1: S_{k+1} on the matrix cores with the exponentials of chunk k
         // (stale stage when k+1 == total; the result is unused then)
         qk(std::integral_constant<int, kst ^ 1>{}, sn0, sn1, s0, s1, m_new, true);
-        rescale(acc, alpha);
 
         // phase 2: O^T += V^T P^T for chunk k with the row sum
         float sum = 0.f;

@@ -53,3 +53,22 @@ def test_block_entries_expand_to_their_keys():
     # blocks in ascending order with every chunk executed: the whole history is covered
     r = _run(lambda o, a, bn: np.arange(a // bn, dtype=np.int32), n_chunks=256 // 64, lists="tile_blocks")
     assert r["coverage"] == 1.0 and r["overlap"] == 1.0
+
+
+def test_refine_tau_brackets_the_budget():
+    # a monotone MSE curve: mse(tau) = tau**2, budget 1e-6 -> boundary at 1e-3
+    curve = lambda t: {"tau": t, "mse": t * t}
+    sweep = [curve(t) for t in (1e-2, 2e-3, 5e-4, 0.0)]
+    tau = bench.refine_tau(sweep, curve, budget=1e-6, steps=6)
+    assert 5e-4 < tau <= 1e-3
+    assert tau > 1e-3 * (2e-3 / 5e-4) ** (-1.0 / 64) * 0.999  # within one final bisection step
+    assert all(r["mse"] <= 1e-6 for r in sweep if r.get("refined") and r["tau"] == tau)
+    assert sum(1 for r in sweep if r.get("refined")) == 6
+
+
+def test_refine_tau_without_bracket():
+    curve = lambda t: {"tau": t, "mse": t * t}
+    sweep = [curve(t) for t in (1e-4, 0.0)]  # every value within budget: nothing to refine
+    assert bench.refine_tau(sweep, curve, budget=1e-6) == 1e-4
+    sweep = [curve(t) for t in (1e-2, 5e-3)]  # none within budget
+    assert bench.refine_tau(sweep, curve, budget=1e-6) is None

@@ -21,13 +21,16 @@
 //      runs of (key, position) pairs).  Within a bucket, positions ascend.
 //   2. range sort.  Each workgroup owns the buckets that start inside its
 //      chunk of C output positions, i.e. a contiguous range of the list, and
-//      sorts it by key with stable 8-bit LSD passes held in LDS.  Keys are
-//      taken relative to the range's minimum and only the bytes that differ
-//      inside the range get a pass (typically three).  Stability and the
-//      ascending positions left by pass 1 give ties to the lower position.
-//      A range larger than the LDS capacity (heavily repeated or clustered
-//      scores) is queued and sorted afterwards by one workgroup with LSD
-//      passes through global scratch, chunk by chunk in order: slower, exact.
+//      orders it without radix passes: NSB sub-buckets of equal score width
+//      over the range (LDS atomics count them, a scan places them), then each
+//      entry's rank inside its sub-bucket is counted by comparing (key,
+//      position) with the few entries sharing it.  A range whose sub-buckets
+//      are too full (clustered or repeated scores) or that exceeds the LDS
+//      capacity is queued.  The queue is drained afterwards: ranges that fit
+//      in LDS by stable 8-bit LSD passes there (keys relative to the range's
+//      minimum, only the bytes that differ), larger ones by LSD passes through
+//      global scratch, chunk by chunk in order: slower, exact.  Stability and
+//      the ascending positions left by pass 1 give ties to the lower position.
 // When no list is longer than the LDS capacity (block lists, short sequences)
 // one workgroup sorts each whole list in LDS and no workspace is used.
 #include "s2o_internal.h"
@@ -45,6 +48,10 @@ constexpr int MAX_CHUNK = 2048;  // output positions owned by a range-sort workg
 constexpr int CAP = 4096;        // entries a range-sort workgroup holds in LDS
 constexpr int CAP_ROUNDS = CAP / THREADS;
 constexpr int OVERFLOW_GRID = 1024;  // workgroups draining the overflow queue
+constexpr int NSB = 1536;        // value-linear sub-buckets of a range (LDS: 4 ranges per CU)
+constexpr int SUB_LIMIT = 32;    // largest sub-bucket ranked by direct comparison
+static_assert(NSB % (4 * THREADS) == 0 || NSB % THREADS == 0, "sub-bucket scan: whole counters per thread");
+static_assert(NSB + 1 >= NWAVES * NB, "the LSD fallback reuses the sub-bucket counters");
 static_assert(THREADS == NB, "the in-LDS passes give each thread one digit");
 static_assert(NWAVES * NB == 4 * THREADS, "counter clear: four per thread");
 
@@ -473,14 +480,136 @@ __device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out
         if (wbase + 64 * r < m) out[wbase + 64 * r] = pos[r];
 }
 
-// An oversized range, queued for overflow_kernel.
+// Inverse of desc_key: the score a key stands for (-0.0 comes back as +0.0).
+__device__ inline float key_score(uint32_t key) {
+    const uint32_t asc = ~key;
+    return __uint_as_float((asc & 0x80000000u) ? (asc & 0x7FFFFFFFu) : ~asc);
+}
+
+// Sorts the m <= R*THREADS entries of one range and writes their positions,
+// without radix passes: every entry goes to one of NSB sub-buckets of equal
+// score width between the range's extremes (highest scores first; the map is
+// monotone in the key, so sub-buckets hold contiguous runs of the order),
+// counted with LDS atomics and placed by an exclusive scan; an entry's final
+// rank is its sub-bucket's start plus the number of entries of its sub-bucket
+// that precede it in (key, position) order.  The result is the unique sorted
+// order, whatever order the atomics hand out slots in.  Returns false, having
+// written nothing, when some sub-bucket holds more than SUB_LIMIT entries
+// (clustered or repeated scores); the caller then sorts the range otherwise.
+template <int R>
+__device__ __forceinline__ bool rank_in_sub_buckets(const u32x2 *__restrict__ in, int32_t *__restrict__ out,
+                                                    int m, u32x2 *stage, int *sbc, int *red) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wbase = wave * R * 64 + lane;
+    // Padding entries (index >= m) take the same steps without branches: they
+    // count into sbc[NSB], land in the stage's tail [m, R*THREADS) and write nothing.
+    u32x2 e[R];
+    int dig[R], slot[R];
+    uint32_t kmin = 0xFFFFFFFFu, nkmax = 0xFFFFFFFFu;  // nkmax = ~(largest key)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = wbase + 64 * r;
+        const bool real = i < m;
+        const u32x2 v = in[real ? i : m - 1];  // in bounds for every lane, no branch
+        e[r].x = real ? v.x : 0xFFFFFFFFu;
+        e[r].y = real ? v.y : 0u;
+        kmin = min(kmin, e[r].x);
+        nkmax = min(nkmax, real ? ~v.x : 0xFFFFFFFFu);
+    }
+    for (int i = tid; i <= NSB; i += THREADS) sbc[i] = 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+        nkmax = min(nkmax, (uint32_t)__shfl_xor((int)nkmax, o));
+    }
+    if (lane == 0) {
+        red[wave] = (int)kmin;
+        red[NWAVES + wave] = (int)nkmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) {
+        kmin = min(kmin, (uint32_t)red[w]);
+        nkmax = min(nkmax, (uint32_t)red[NWAVES + w]);
+    }
+    // sub-bucket of a score: floor((top - x) * NSB / (top - bottom)), clamped;
+    // a single sub-bucket when the width is zero, not finite or too small to divide by
+    const float top = key_score(kmin), width = top - key_score(~nkmax);
+    const float scale = (float)NSB / width;
+    const bool spread = width > 0.f && width < INFINITY && scale < INFINITY;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int d = spread ? min((int)((top - key_score(e[r].x)) * scale), NSB - 1) : 0;
+        dig[r] = wbase + 64 * r < m ? d : NSB;
+        slot[r] = atomicAdd(&sbc[dig[r]], 1);
+    }
+    __syncthreads();
+    // exclusive scan of the counts in place (sbc[NSB] = m), and the largest count
+    {
+        constexpr int PER = NSB / THREADS;
+        int c[PER];
+        int tot = 0, cmax = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            c[k] = sbc[tid * PER + k];
+            tot += c[k];
+            cmax = max(cmax, c[k]);
+        }
+        int incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int x = __shfl_up(incl, o);
+            if (lane >= o) incl += x;
+            cmax = max(cmax, __shfl_xor(cmax, o));
+        }
+        if (lane == 63) red[2 * NWAVES + wave] = incl;
+        if (lane == 0) red[3 * NWAVES + wave] = cmax;
+        __syncthreads();
+        int base = 0;
+        cmax = 0;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) {
+            base += w < wave ? red[2 * NWAVES + w] : 0;
+            cmax = max(cmax, red[3 * NWAVES + w]);
+        }
+        if (cmax > SUB_LIMIT) return false;  // the same on every thread
+        int run = base + incl - tot;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            sbc[tid * PER + k] = run;
+            run += c[k];
+        }
+        if (tid == THREADS - 1) sbc[NSB] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) stage[sbc[dig[r]] + slot[r]] = e[r];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int d = dig[r];
+        const int b0 = sbc[d], b1 = d < NSB ? sbc[d + 1] : b0;
+        int rank = b0;
+        if (b1 - b0 > 1) {
+            for (int j = b0; j < b1; ++j) {
+                const u32x2 o = stage[j];
+                rank += (o.x < e[r].x || (o.x == e[r].x && o.y < e[r].y)) ? 1 : 0;
+            }
+        }
+        if (d < NSB) out[rank] = (int32_t)e[r].y;
+    }
+    return true;
+}
+
+// A range queued for overflow_kernel.
 struct Overflow {
     int32_t lid, rs, m;
 };
 
 // One workgroup per chunk of C output positions of a list: sorts the buckets
 // that start inside the chunk (see the file comment) and writes positions.
-// A range larger than CAP is queued for overflow_kernel instead.
+// A range larger than CAP, or with a sub-bucket fuller than SUB_LIMIT, is
+// queued for overflow_kernel instead.
 template <int C>
 __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__restrict__ pairs,
                                                                 int32_t *__restrict__ idx,
@@ -490,9 +619,9 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
                                                                 int32_t *__restrict__ queue_len,
                                                                 Geometry g, int E) {
     __shared__ u32x2 stage[CAP];
-    __shared__ int cnt[NWAVES][NB];
-    __shared__ uint32_t red[NWAVES];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    __shared__ int sbc[NSB + 1];
+    __shared__ int sred[4 * NWAVES];
+    const int tid = threadIdx.x;
     const int64_t e0 = (int64_t)blockIdx.x * C;
     const int lid = blk_list[e0 / E];
     const ListRef L = list_ref(g, lid);
@@ -509,10 +638,12 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
     }
     const u32x2 *in = pairs + L.off + rs;
     int32_t *out = idx + L.off + rs;
-    auto load = [in](int i) { return in[i]; };
     switch ((m + THREADS - 1) / THREADS) {  // one instantiation per round count
-#define S2O_SORT_CASE(R) \
-    case R: sort_in_lds<R>(load, out, m, stage, cnt, red); break;
+#define S2O_SORT_CASE(R)                                                   \
+    case R:                                                                \
+        if (!rank_in_sub_buckets<R>(in, out, m, stage, sbc, sred) && tid == 0) \
+            queue[atomicAdd(queue_len, 1)] = {lid, rs, m};                     \
+        break;
         S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
         S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
         S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
@@ -552,15 +683,17 @@ __global__ __launch_bounds__(THREADS, 4) void list_sort_kernel(const float *__re
     }
 }
 
-// Oversized ranges (heavily repeated or clustered scores): each workgroup
-// takes queued ranges in turn and sorts one with stable LSD passes through
-// global scratch, CAP entries at a time in order.
+// Queued ranges (clustered, repeated or very many scores): each workgroup
+// takes queued ranges in turn; one that fits in LDS is sorted there with
+// stable LSD passes, a larger one with stable LSD passes through global
+// scratch, CAP entries at a time in order.
 __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ pairs,
                                                            u32x2 *__restrict__ scratch,
                                                            int32_t *__restrict__ idx,
                                                            const Overflow *__restrict__ queue,
                                                            const int32_t *__restrict__ queue_len,
                                                            Geometry g) {
+    __shared__ u32x2 stage[CAP];
     __shared__ int cnt[NWAVES][NB];
     __shared__ int dtot[NB];
     __shared__ int run[NB];
@@ -574,6 +707,22 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
         const Overflow ov = queue[q];
         const int64_t base = list_ref(g, ov.lid).off + ov.rs;
         const int m = ov.m;
+        if (m <= CAP) {  // fits in LDS: stable LSD passes there
+            const u32x2 *in = pairs + base;
+            auto load = [in](int i) { return in[i]; };
+            switch ((m + THREADS - 1) / THREADS) {
+#define S2O_SORT_CASE(R) \
+    case R: sort_in_lds<R>(load, idx + base, m, stage, cnt, red); break;
+                S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
+                S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
+                S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
+                S2O_SORT_CASE(13) S2O_SORT_CASE(14) S2O_SORT_CASE(15) S2O_SORT_CASE(16)
+#undef S2O_SORT_CASE
+                default: break;
+            }
+            __syncthreads();  // the next range reuses the LDS
+            continue;
+        }
         u32x2 *src = pairs + base, *dst = scratch + base;
         uint32_t kmin = 0xFFFFFFFFu;
         for (int i = tid; i < m; i += THREADS) kmin = min(kmin, src[i].x);

@@ -261,19 +261,33 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
         }
     }
 
-    auto unit_of = [&](int pp, int &hq, int &t) -> const float * {
-        hq = pp / ntiles;
-        t = t_first + pp - hq * ntiles;
-        return g.per_seg ? qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.nseg + s) * D
-                         : qbar + (((int64_t)b * g.Hq + kvh * g.G + hq) * g.T + t) * D;
+    // Pair pp -> (query head kvh*G + hq, tile t_first + ti), hq = pp / ntiles by a
+    // multiply-high with ceil(2^32 / ntiles) (exact while pp * ntiles < 2^32,
+    // else a plain division), and
+    // the pair's pooled query and list position in closed form (the tiles of
+    // one head are consecutive in both layouts; the list of tile t_first + ti
+    // starts ti * S * s after the segment's first list).
+    const uint32_t magic = ntiles > 1 ? (uint32_t)((0x100000000ull + ntiles - 1) / (uint64_t)ntiles) : 0u;
+    const bool by_magic = (int64_t)npairs * ntiles < 0x100000000ll;
+    const int qrows = g.per_seg ? g.nseg : g.T;  // pooled queries per head
+    const float *qhead0 = qbar + (((int64_t)b * g.Hq + kvh * g.G) * qrows + (g.per_seg ? s : t_first)) * D;
+    const int64_t L = g.list_per_head;
+    const int64_t seg_first = g.per_seg ? (int64_t)g.S * (s * (s - 1) / 2)
+                                        : (int64_t)g.S * ((int64_t)g.P * s * (s - 1) / 2);
+    float *shead0 = scores + ((int64_t)b * g.Hq + kvh * g.G) * L + seg_first + j;
+    const int64_t tile_step = g.per_seg ? 0 : (int64_t)g.S * s;
+    auto split = [&](int pp, int &hq, int &ti) {
+        hq = ntiles == 1 ? pp : by_magic ? (int)__umulhi((uint32_t)pp, magic) : pp / ntiles;
+        ti = pp - hq * ntiles;
     };
     // q[i][c] = pooled query of pair p0 + i, element 16c + col (every row alike),
     // read as NQ contiguous floats of the lane-major layout
     auto load_group = [&](float (&q)[SCORE_ILP][NQ], int p0) {
 #pragma unroll
         for (int i = 0; i < SCORE_ILP; ++i) {
-            int hq, t;
-            const float *src = unit_of(min(p0 + i, npairs - 1), hq, t) + col * NQ;
+            int hq, ti;
+            split(min(p0 + i, npairs - 1), hq, ti);
+            const float *src = qhead0 + ((int64_t)hq * qrows + ti) * D + col * NQ;
 #pragma unroll
             for (int c = 0; c < NQ; c += 4) {
                 const float4 v = *reinterpret_cast<const float4 *>(src + c);
@@ -288,9 +302,9 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
 #pragma unroll
         for (int i = 0; i < SCORE_ILP; ++i) {
             if (live && p0 + i < npairs) {
-                int hq, t;
-                unit_of(p0 + i, hq, t);
-                scores[list_offset(g, b, kvh * g.G + hq, t) + j] = acc[i];
+                int hq, ti;
+                split(p0 + i, hq, ti);
+                shead0[hq * L + ti * tile_step] = acc[i];
             }
         }
     };

@@ -18,7 +18,10 @@
 //      scores share a bucket.  minmax (per block) -> hist (per block, LDS
 //      atomics) -> scan (per list) -> scatter (per block: stable rank by a
 //      wave-level multisplit, staged in LDS, written as contiguous bucket
-//      runs of (key, position) pairs).  Within a bucket, positions ascend.
+//      runs of (key, position) pairs).  Within a bucket, positions ascend;
+//      the steps below do not rely on it (the multisplit is kept because LDS
+//      atomics on the few crowded buckets of a peaked score distribution
+//      serialize and cost more than it).
 //   2. range sort.  Each workgroup owns the buckets that start inside its
 //      chunk of C output positions, i.e. a contiguous range of the list, and
 //      orders it without radix passes: NSB sub-buckets of equal score width
@@ -26,11 +29,11 @@
 //      entry's rank inside its sub-bucket is counted by comparing (key,
 //      position) with the few entries sharing it.  A range whose sub-buckets
 //      are too full (clustered or repeated scores) or that exceeds the LDS
-//      capacity is queued.  The queue is drained afterwards: ranges that fit
-//      in LDS by stable 8-bit LSD passes there (keys relative to the range's
-//      minimum, only the bytes that differ), larger ones by LSD passes through
-//      global scratch, chunk by chunk in order: slower, exact.  Stability and
-//      the ascending positions left by pass 1 give ties to the lower position.
+//      capacity is queued.  The queue is drained afterwards by stable 8-bit
+//      LSD passes over the bytes of the position, then of the key, that vary
+//      inside the range (both taken relative to the range's lowest value): in
+//      LDS when the range fits, else through global scratch, chunk by chunk in
+//      order.  Slower, exact, and ordered by (key, position) like the rest.
 // When no list is longer than the LDS capacity (block lists, short sequences)
 // one workgroup sorts each whole list in LDS and no workspace is used.
 #include "s2o_internal.h"
@@ -383,46 +386,57 @@ __device__ inline uint32_t block_or(uint32_t x, uint32_t *sh) {
 
 // Sorts the m <= R*THREADS entries of one range in LDS and writes their
 // positions: stable 8-bit LSD passes on the key relative to the range minimum,
-// only over the bytes that vary.  Padding entries (rel = all ones) stay last.
-// load(i) gives entry i as (key, position).
-template <int R, typename Load>
+// only over the bytes that vary.  With BY_POS the passes on the key are
+// preceded by passes on the position relative to the range's lowest one, so
+// the result is ordered by (key, position) whatever the input order; without
+// it the input must list equal keys by ascending position.  Padding entries
+// (all ones in both) stay last.  load(i) gives entry i as (key, position).
+template <int R, bool BY_POS, typename Load>
 __device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out, int m, u32x2 *stage,
                                             int (*cnt)[NB], uint32_t *red) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wbase = wave * R * 64 + lane;
     uint32_t rel[R];
-    int32_t pos[R];
+    uint32_t prel[R];  // position relative to the lowest one
     int rank[R];
-    uint32_t kmin = 0xFFFFFFFFu;
+    uint32_t kmin = 0xFFFFFFFFu, pmin = 0xFFFFFFFFu;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int i = wbase + 64 * r;
         u32x2 pr;
         pr.x = 0xFFFFFFFFu;
-        pr.y = 0;
+        pr.y = 0xFFFFFFFFu;
         if (i < m) pr = load(i);
         rel[r] = pr.x;
-        pos[r] = (int32_t)pr.y;
+        prel[r] = pr.y;
         kmin = min(kmin, pr.x);
+        pmin = min(pmin, pr.y);
     }
     kmin = block_min(kmin, red);
-    uint32_t span = 0;
+    if (BY_POS) pmin = block_min(pmin, red);
+    uint32_t span = 0, pspan = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const bool real = wbase + 64 * r < m;
         rel[r] = real ? rel[r] - kmin : 0xFFFFFFFFu;
         span |= real ? rel[r] : 0u;
+        if (BY_POS) {
+            prel[r] = real ? prel[r] - pmin : 0xFFFFFFFFu;
+            pspan |= real ? prel[r] : 0u;
+        }
     }
     span = block_or(span, red);
-    for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 8 * pass;
-        if (((span >> shift) & 0xFFu) == 0) continue;  // digit constant in the range
+    if (BY_POS) pspan = block_or(pspan, red);
+    for (int pass = BY_POS ? 0 : 4; pass < 8; ++pass) {
+        const bool on_pos = pass < 4;  // position bytes first, then key bytes
+        const int shift = 8 * (pass & 3);
+        if ((((on_pos ? pspan : span) >> shift) & 0xFFu) == 0) continue;  // digit constant in the range
         // per-wave digit counters: zero, count with stable in-wave ranks
         *reinterpret_cast<int4 *>(&cnt[0][0] + 4 * threadIdx.x) = int4{0, 0, 0, 0};
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint32_t d = (rel[r] >> shift) & 0xFFu;
+            const uint32_t d = ((on_pos ? prel[r] : rel[r]) >> shift) & 0xFFu;
             const uint64_t peers = match_digit(d);
             const int before = cnt[wave][d];
             rank[r] = before + __popcll(peers & lanemask_lt());
@@ -460,10 +474,10 @@ __device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out
         // stage (key, position) pairs sorted by the digit: one read, one 8-byte write
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint32_t d = (rel[r] >> shift) & 0xFFu;
+            const uint32_t d = ((on_pos ? prel[r] : rel[r]) >> shift) & 0xFFu;
             u32x2 pr;
             pr.x = rel[r];
-            pr.y = (uint32_t)pos[r];
+            pr.y = prel[r];
             stage[cnt[wave][d] + rank[r]] = pr;
         }
         __syncthreads();
@@ -472,12 +486,12 @@ __device__ __forceinline__ void sort_in_lds(Load load, int32_t *__restrict__ out
         for (int r = 0; r < R; ++r) {
             const u32x2 pr = stage[wbase + 64 * r];
             rel[r] = pr.x;
-            pos[r] = (int32_t)pr.y;
+            prel[r] = pr.y;
         }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        if (wbase + 64 * r < m) out[wbase + 64 * r] = pos[r];
+        if (wbase + 64 * r < m) out[wbase + 64 * r] = (int32_t)(prel[r] + (BY_POS ? pmin : 0u));
 }
 
 // Inverse of desc_key: the score a key stands for (-0.0 comes back as +0.0).
@@ -673,7 +687,7 @@ __global__ __launch_bounds__(THREADS, 4) void list_sort_kernel(const float *__re
     };
     switch ((m + THREADS - 1) / THREADS) {
 #define S2O_SORT_CASE(R) \
-    case R: sort_in_lds<R>(load, out, m, stage, cnt, red); break;
+    case R: sort_in_lds<R, false>(load, out, m, stage, cnt, red); break;
         S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
         S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
         S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
@@ -700,7 +714,7 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
     __shared__ uint32_t red[NWAVES];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nq = *queue_len;
-    uint32_t rel[CAP_ROUNDS];
+    uint32_t rel[CAP_ROUNDS], key[CAP_ROUNDS];
     int32_t pos[CAP_ROUNDS];
     int rank[CAP_ROUNDS];
     for (int q = blockIdx.x; q < nq; q += gridDim.x) {
@@ -712,7 +726,7 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
             auto load = [in](int i) { return in[i]; };
             switch ((m + THREADS - 1) / THREADS) {
 #define S2O_SORT_CASE(R) \
-    case R: sort_in_lds<R>(load, idx + base, m, stage, cnt, red); break;
+    case R: sort_in_lds<R, true>(load, idx + base, m, stage, cnt, red); break;
                 S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
                 S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
                 S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
@@ -724,18 +738,29 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
             continue;
         }
         u32x2 *src = pairs + base, *dst = scratch + base;
-        uint32_t kmin = 0xFFFFFFFFu;
-        for (int i = tid; i < m; i += THREADS) kmin = min(kmin, src[i].x);
+        uint32_t kmin = 0xFFFFFFFFu, pmin = 0xFFFFFFFFu;
+        for (int i = tid; i < m; i += THREADS) {
+            kmin = min(kmin, src[i].x);
+            pmin = min(pmin, src[i].y);
+        }
         kmin = block_min(kmin, red);
-        uint32_t span = 0;
-        for (int i = tid; i < m; i += THREADS) span |= src[i].x - kmin;
+        pmin = block_min(pmin, red);
+        uint32_t span = 0, pspan = 0;
+        for (int i = tid; i < m; i += THREADS) {
+            span |= src[i].x - kmin;
+            pspan |= src[i].y - pmin;
+        }
         span = block_or(span, red);
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 8 * pass;
-            if (((span >> shift) & 0xFFu) == 0) continue;
+        pspan = block_or(pspan, red);
+        // position bytes first, then key bytes: ordered by (key, position)
+        for (int pass = 0; pass < 8; ++pass) {
+            const bool on_pos = pass < 4;
+            const int shift = 8 * (pass & 3);
+            if ((((on_pos ? pspan : span) >> shift) & 0xFFu) == 0) continue;
+            auto value = [&](u32x2 pr) { return on_pos ? pr.y - pmin : pr.x - kmin; };
             for (int v = tid; v < NB; v += THREADS) run[v] = 0;
             __syncthreads();
-            for (int i = tid; i < m; i += THREADS) atomicAdd(&run[((src[i].x - kmin) >> shift) & 0xFFu], 1);
+            for (int i = tid; i < m; i += THREADS) atomicAdd(&run[(value(src[i]) >> shift) & 0xFFu], 1);
             __syncthreads();
             scan256(run);
             __syncthreads();
@@ -749,10 +774,12 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
                         const int i = wbase + 64 * r;
                         if (i < cm) {
                             const u32x2 pr = src[c0 + i];
-                            rel[r] = pr.x - kmin;
+                            rel[r] = value(pr);
+                            key[r] = pr.x;
                             pos[r] = (int32_t)pr.y;
                         } else {
                             rel[r] = 0xFFFFFFFFu;
+                            key[r] = 0;
                             pos[r] = 0;
                         }
                     }
@@ -763,13 +790,13 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
                     if (r < rounds && wbase + 64 * r < cm) {
                         const uint32_t d = (rel[r] >> shift) & 0xFFu;
                         u32x2 pr;
-                        pr.x = rel[r] + kmin;
+                        pr.x = key[r];
                         pr.y = (uint32_t)pos[r];
                         dst[run[d] + cnt[wave][d] + rank[r]] = pr;
                     }
                 }
                 __syncthreads();
-                // padding entries (rel = all ones, digit 0xFF in every pass) rank after
+                // padding entries (all ones, digit 0xFF in every pass) rank after
                 // every real entry of digit 0xFF and are neither written nor counted
                 for (int v = tid; v < NB; v += THREADS) run[v] += dtot[v] - (v == 0xFF ? rounds * THREADS - cm : 0);
                 __syncthreads();

@@ -349,6 +349,8 @@ def _crafted_scores(kind, n, rng):
         s[::1009] = np.float32(-3e38)
         s[::31] = np.float32(1e-40)    # denormals
         return s
+    if kind == "many_ties":            # ~120 copies of each of 200 values: ranges fit in LDS,
+        return rng.integers(0, 200, n).astype(np.float32)  # their sub-buckets overflow
     if kind == "gaussian_ties":        # the usual case, with exact ties mixed in
         s = (rng.standard_normal(n) * 4).astype(np.float32)
         s[::5] = np.round(s[::5])
@@ -358,7 +360,7 @@ def _crafted_scores(kind, n, rng):
 
 @pytest.mark.parametrize("lists", ["tile", "segment"])
 @pytest.mark.parametrize("kind", ["all_equal", "signed_zeros", "few_values", "outlier",
-                                  "extreme_range", "gaussian_ties"])
+                                  "extreme_range", "many_ties", "gaussian_ties"])
 def test_build_index_crafted_scores(kind, lists):
     """s2o_build_index on score arrays that force oversized buckets, exact ties,
     signed zeros, denormals and an overflowing score range, against the oracle's

@@ -607,6 +607,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     const int n2 = S2O ? seg_a / BN : 0;
     const int total = n1 + n2;
     const int32_t *list = S2O ? a.idx + list_offset(g, b, h, t) : nullptr;
+    // this tile's list as a buffer resource: 32-bit offsets per entry load
+    const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)list, (short)0, S2O ? (int)((g.blocks ? seg_a / BN : seg_a) * 4) : 0, 0x00020000);
 
     const int kvh = h / g.G;
     const __bf16 *Qp = reinterpret_cast<const __bf16 *>(a.q) + ((int64_t)(b * g.Hq + h) * g.N) * D;
@@ -629,19 +632,27 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
 #pragma unroll
             for (int i = 0; i < C::INSTR; ++i) rows[i] = first + slot_row(i);
         } else {
-            const int32_t *entries = list + (int64_t)(k - n1) * BN;
+            const int first = (k - n1) * BN;
 #pragma unroll
-            for (int i = 0; i < C::INSTR; ++i) rows[i] = entries[slot_row(i)];
+            for (int i = 0; i < C::INSTR; ++i)
+                rows[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(lrs, (unsigned)((first + slot_row(i)) * 4), 0, 0);
         }
     };
+    // K and V of this KV head as buffer resources: 32-bit byte offsets per lane,
+    // the LDS destination from a scalar base (the wave index made uniform), and
+    // reads past the head's rows return zeros instead of touching other memory
+    const int head_bytes = g.N * D * 2;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)Kp, (short)0, head_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)Vp, (short)0, head_bytes, 0x00020000);
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     auto issue_k = [&](int stage, const int (&rows)[C::INSTR]) {
 #pragma unroll
         for (int i = 0; i < C::INSTR; ++i) {
             const int r = slot_row(i);
             const int c = slot_col(i) ^ kswz<D>(r);
-            __builtin_amdgcn_global_load_lds(Kp + (int64_t)rows[i] * D + c * 8,
-                                             (lds_void *)(lds + stage * C::TILEB + (wave * C::INSTR + i) * 1024),
-                                             16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                krs, (lds_void *)(lds + stage * C::TILEB + (wave_s * C::INSTR + i) * 1024), 16,
+                (unsigned)(rows[i] * C::ROWB + c * 16), 0, 0, 0);
         }
     };
     auto issue_v = [&](int stage, const int (&rows)[C::INSTR]) {
@@ -649,9 +660,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         for (int i = 0; i < C::INSTR; ++i) {
             const int r = slot_row(i);
             const int c = slot_col(i) ^ vswz<D>(r);
-            __builtin_amdgcn_global_load_lds(Vp + (int64_t)rows[i] * D + c * 8,
-                                             (lds_void *)(lds + (2 + stage) * C::TILEB + (wave * C::INSTR + i) * 1024),
-                                             16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                vrs, (lds_void *)(lds + (2 + stage) * C::TILEB + (wave_s * C::INSTR + i) * 1024), 16,
+                (unsigned)(rows[i] * C::ROWB + c * 16), 0, 0, 0);
         }
     };
 
@@ -768,7 +779,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         qk(std::integral_constant<int, kst ^ 1>{}, sn0, sn1, s0, s1, m_new, true);
 
         // phase 2: O^T += V^T P^T for chunk k with the row sum
-        float sum = 0.f;
+        float sum;
         {
             const unsigned char *Vt = lds + (2 + kst) * C::TILEB;
             bf16x8 pb[4];
@@ -792,7 +803,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
                     acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sum += s0[4 * s + e] + s1[4 * s + e];
+                for (int e = 0; e < 4; ++e) {
+                    const float pair = s0[4 * s + e] + s1[4 * s + e];
+                    sum = (s == 0 && e == 0) ? pair : sum + pair;  // no leading + 0
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }

@@ -2,8 +2,11 @@
 
 Usage: python -m long_context_prefill_amd.profile_summary KERNEL_STATS_CSV
            [--fetch COUNTER_CSV --write COUNTER_CSV --copy-bytes N] --command "..."
+       python -m long_context_prefill_amd.profile_summary --counters CSV [CSV ...] --command "..."
 Counter values (FETCH_SIZE, WRITE_SIZE, in KiB per dispatch) are scaled by what
 the same counter reads for the plain copy kernel of known size in the same run.
+--counters averages SQ counters per dispatch for the attention kernels and
+derives matrix-core and wave-state shares from them (see counter_report).
 """
 
 from __future__ import annotations
@@ -12,6 +15,7 @@ import argparse
 import collections
 import csv
 import json
+import sys
 
 
 def short(name: str) -> str:
@@ -42,7 +46,64 @@ def per_kernel(path, value="Counter_Value"):
     return agg
 
 
+# MI355X: 256 CUs x 4 SIMDs in 32 shader engines.  SQ_BUSY_CYCLES sums the
+# busy cycles of every shader engine; SQ_VALU_MFMA_BUSY_CYCLES and
+# SQ_VALU_MFMA_COEXEC_CYCLES sum SIMD cycles; the SQ_WAVE_CYCLES / SQ_WAIT_* /
+# SQ_ACTIVE_INST_ANY family sums wave cycles (in the same unit, so only their
+# ratios are used).
+SIMDS, SHADER_ENGINES = 1024, 32
+
+
+def counter_report(paths):
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            n = short(r["Kernel_Name"])
+            if n in ("s2o_attn_fwd (S2O schedule)", "dense_attn_fwd"):
+                per[n][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    for n, cs in per.items():
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        simd_cycles = avg["SQ_BUSY_CYCLES"] / SHADER_ENGINES * SIMDS
+        wave = avg["SQ_WAVE_CYCLES"]
+        out[n] = {
+            "counters": avg,
+            "mfma_busy": avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles,
+            "mfma_valu_coexec": avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd_cycles,
+            "wave_issuing": avg["SQ_ACTIVE_INST_ANY"] / wave,
+            "wave_waiting_issue": avg["SQ_WAIT_INST_ANY"] / wave,
+            "wave_waiting_counters_barrier": avg["SQ_WAIT_ANY"] / wave,
+            "valu_insts_per_mfma": (avg["SQ_INSTS_VALU"] - avg["SQ_INSTS_MFMA"]) / avg["SQ_INSTS_MFMA"],
+            "trans_per_mfma": avg["SQ_INSTS_VALU_TRANS_F32"] / avg["SQ_INSTS_MFMA"],
+            "lds_insts_per_mfma": avg["SQ_INSTS_LDS"] / avg["SQ_INSTS_MFMA"],
+        }
+    return out
+
+
+def main_counters(a):
+    print(f"command: {a.command}\n")
+    rep = counter_report(a.counters)
+    for n, r in rep.items():
+        print(f"{n}: per dispatch")
+        for c, v in sorted(r["counters"].items()):
+            print(f"  {c:32s} {v:14.4g}")
+        print(f"  matrix cores busy                {100 * r['mfma_busy']:6.1f} % of SIMD cycles "
+              f"(SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES / {SHADER_ENGINES} x {SIMDS}))")
+        print(f"  vector and matrix co-issuing     {100 * r['mfma_valu_coexec']:6.1f} % of SIMD cycles")
+        print(f"  wave time issuing / waiting for an issue slot / at waits and barriers: "
+              f"{100 * r['wave_issuing']:.0f} / {100 * r['wave_waiting_issue']:.0f} / "
+              f"{100 * r['wave_waiting_counters_barrier']:.0f} %")
+        print(f"  per MFMA: {r['valu_insts_per_mfma']:.2f} other VALU ({r['trans_per_mfma']:.2f} "
+              f"transcendental), {r['lds_insts_per_mfma']:.2f} LDS instructions\n")
+
+
 def main():
+    if "--counters" in sys.argv:
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--counters", nargs="+", required=True)
+        ap.add_argument("--command", required=True)
+        main_counters(ap.parse_args())
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("stats")
     ap.add_argument("--fetch")

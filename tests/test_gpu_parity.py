@@ -217,7 +217,8 @@ def test_llama8b_128k_sampled():
     x = synth.make_inputs(w)
     run = GpuRun(w, x)
     tiles = sample_tiles(w, heads=(0, 27), n_random=8, seed=3)
-    for tau in (1e-3, 1e-2):
+    # 1.42e-3: about the tau bench.py settles on for this workload (MSE <= 1e-5)
+    for tau in (1e-3, 1.42e-3, 1e-2):
         o, ex = run.attn(tau)
         say(f"oracle on {len(tiles)} sampled tiles")
         rep = compare(run, tiles, tau, o, ex, check_lists=(tau == 1e-3))

@@ -100,12 +100,15 @@ __device__ inline float max16(const f32x16 &v) {
 
 // Causal mask on a diagonal chunk.  Register r of block blk holds key
 // key0 + 32*blk + 8*(r/4) + 4*half + r%4 for this lane's query row.
+// Key kk is masked when kk > row, i.e. when its compile-time part
+// 8*(r/4) + r%4 (+32) exceeds the lane's row - key0 - 4*half.
 __device__ inline void mask_chunk(f32x16 &s0, f32x16 &s1, int key0, int row, int half) {
+    const int lim = row - key0 - 4 * half;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        int kk = key0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (kk > row) s0[r] = -INFINITY;
-        if (kk + 32 > row) s1[r] = -INFINITY;
+        const int kr = 8 * (r >> 2) + (r & 3);
+        s0[r] = kr > lim ? -INFINITY : s0[r];
+        s1[r] = kr + 32 > lim ? -INFINITY : s1[r];
     }
 }
 

@@ -119,6 +119,12 @@ __device__ inline void mask_chunk(f32x16 &s0, f32x16 &s1, int key0, int row, int
 // below 2^kMaxSlack, and since l, delta and acc all use the same m the result
 // (acc / l, delta / l) is unchanged while most chunks skip the rescale.
 constexpr float kMaxSlack = 8.0f;
+// Headroom (log2 units) between chunk 0's row max and the fixed reference of
+// the bf16 kernel's first attempt: later logits may exceed that max by up to
+// kFastHeadroom + 58 before a chunk's mass reaches the 2^64 check; logits more
+// than 126 - kFastHeadroom below it underflow, negligible against the row's
+// chunk-0 mass (>= 2^-kFastHeadroom).
+constexpr float kFastHeadroom = 60.0f;
 
 __device__ inline void softmax_chunk(f32x16 &s0, f32x16 &s1, float c, float &m, float &l,
                                      float &alpha, float &delta) {
@@ -677,11 +683,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
 
     constexpr int NACC = D / 32;
     f32x16 acc[NACC];
-#pragma unroll
-    for (int i = 0; i < NACC; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-    float m = -INFINITY, l = 0.f;
+    float m, l;
     const float c = a.scale_log2;
 
     // Per-lane LDS byte offsets of the operand reads.  With the stage a
@@ -738,6 +740,27 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         }
     };
 
+    // Running max.  First attempt (track = false): the row max is taken on
+    // chunk 0 only and the reference m is fixed kFastHeadroom above it, so a
+    // chunk costs no max, no rescale test and no rescale; every chunk's mass
+    // is checked against 2^64 instead (at most kFastHeadroom + 58 log2 units
+    // above chunk 0's max; inf and NaN fail the check too), which keeps acc and
+    // l far from overflow.  A failed check restarts the tile with the lazy
+    // running max (track = true).  acc / l and delta / l do not depend on m, so
+    // both attempts compute the same quantities.
+    int executed2 = 0;
+    // one attempt over the tile; returns true when it overflowed
+    auto attempt = [&](auto track_c) -> bool {
+    constexpr bool track = decltype(track_c)::value;
+    bool overflow = false;
+#pragma unroll
+    for (int i = 0; i < NACC; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    m = -INFINITY;
+    l = 0.f;
+    executed2 = 0;
+
     // prologue: K_0, V_0, K_1 into their stages; S_0
     fetch_rows(0, krows);
     issue_k(0, krows);
@@ -755,8 +778,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     __syncthreads();  // every wave has read K stage 0 before it is refilled
 
     // One chunk k whose K/V sit in stage kst; s holds S_k, sn receives S_{k+1}.
-    // Returns false when the tile stops (or the schedule ends) after chunk k.
-    int executed2 = 0;
+    // Returns false when the tile stops (or the schedule ends, or the first
+    // attempt overflows) after chunk k.
     auto iteration = [&](auto kst_c, int k, f32x16 &s0, f32x16 &s1, f32x16 &sn0, f32x16 &sn1) -> bool {
         constexpr int kst = decltype(kst_c)::value;
         if (k + 2 < total) issue_k(kst, krows);            // K_{k+2} -> stage of K_k
@@ -769,17 +792,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         const bool is_p2 = S2O && k >= n1;
         const int key0 = is_p2 ? 0 : base1 + k * BN;
         if (!is_p2 && g.causal && key0 + BN - 1 > wave_first) mask_chunk(s0, s1, key0, my_row, half);
-        const float mx = pair_max(fmaxf(max16(s0), max16(s1))) * c;
-        const float m_new = mx > m + kMaxSlack ? mx : m;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        m = m_new;
-
-        // (before the matrix-core phase: its branch would otherwise split the
-        // exponentials from the products they are meant to overlap)
-        rescale(acc, alpha);
+        float alpha = 1.f;
+        if (track || k == 0) {  // uniform
+            const float mx = pair_max(fmaxf(max16(s0), max16(s1))) * c;
+            const float m_new = !track ? mx + kFastHeadroom : mx > m + kMaxSlack ? mx : m;
+            alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on chunk 0 (m = -inf)
+            m = m_new;
+            // (before the matrix-core phase: its branch would otherwise split
+            // the exponentials from the products they are meant to overlap)
+            if (k > 0) rescale(acc, alpha);
+        }
         // phase 1: S_{k+1} on the matrix cores with the exponentials of chunk k
         // (stale stage when k+1 == total; the result is unused then)
-        qk(std::integral_constant<int, kst ^ 1>{}, sn0, sn1, s0, s1, m_new, true);
+        qk(std::integral_constant<int, kst ^ 1>{}, sn0, sn1, s0, s1, m, true);
 
         // phase 2: O^T += V^T P^T for chunk k with the row sum
         float sum;
@@ -816,16 +841,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         const float delta = pair_sum(sum);
         l = l * alpha + delta;
         const bool wave_cont = is_p2 && __ballot(!(delta < a.tau * l)) != 0;
+        const bool wave_ovf = !track && __ballot(!(delta < 0x1p64f)) != 0;
 
         __builtin_amdgcn_s_waitcnt(0);  // this wave's K_{k+2} / V_{k+1} pieces and indices landed
-        if (is_p2 && lane == 0) flags[kst][wave] = wave_cont ? 1 : 0;
+        if (lane == 0) flags[kst][wave] = (wave_cont ? 1 : 0) | (wave_ovf ? 2 : 0);
         __syncthreads();
+        int any = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) any |= flags[kst][w];
+        if (any & 2) {
+            overflow = true;
+            return false;
+        }
         if (is_p2) {
             executed2 = k - n1 + 1;
-            int any = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) any |= flags[kst][w];
-            if (!any) return false;
+            if (!(any & 1)) return false;
         }
         return k + 1 < total;
     };
@@ -833,6 +863,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         if (!iteration(std::integral_constant<int, 0>{}, k, sa0, sa1, sb0, sb1)) break;
         if (!iteration(std::integral_constant<int, 1>{}, k + 1, sb0, sb1, sa0, sa1)) break;
     }
+    return overflow;
+    };
+    if (attempt(std::false_type{})) attempt(std::true_type{});
 
     const float inv = 1.0f / l;
     __bf16 *Op = reinterpret_cast<__bf16 *>(a.o) + ((int64_t)(b * g.Hq + h) * g.N + my_row) * D;

@@ -88,6 +88,36 @@ def test_small_bf16_every_tile(case):
         assert_report(rep, "bf16")
 
 
+def test_large_logit_jump_restarts_with_running_max():
+    """The bf16 kernels fix their softmax reference after a tile's first chunk
+    and redo the tile with a running max when a later chunk's mass overflows the
+    check.  Two keys carry a 2000x component along the queries' planted
+    direction (logits some 350 nats above the rest): key 40 is met in pass 1 by
+    segment 0 and in the first pass-2 chunk by later segments, key 700 mid-way
+    through pass 1 of segment 2 and of the dense kernel; every tile must still
+    match the oracle."""
+    w = synth.custom_workload(B=1, Hq=2, Hkv=1, N=1024, d=128, dtype="bf16", tile_m=128, tile_n=64,
+                              seg_len=256, structure="stripes", n_stripes=8, seed=901, name="logit_jump")
+    x = synth.make_inputs(w)
+    qf = synth.f32_from_bf16_bits(x["q"])
+    u = qf[0].reshape(-1, w.d).mean(axis=0)
+    u = u / np.linalg.norm(u)
+    k = synth.f32_from_bf16_bits(x["k"]).copy()
+    for j in (40, 700):
+        k[0, 0, j] = 2000.0 * u
+    x["k"] = synth.bf16_bits_from_f32(k)
+    run = GpuRun(w, x)
+    for tau in (0.0, 1e-3):
+        o, ex = run.attn(tau)
+        rep = compare(run, all_tiles(w), tau, o, ex, check_lists=True)
+        assert_report(rep, "bf16")
+    od = f64(run.dense())
+    refs = oracle.dense_requests(run.po, x["q"], x["k"], x["v"], [(0, h, 0, w.N) for h in range(w.Hq)])
+    for h in range(w.Hq):
+        d = np.abs(od[0, h] - refs[h])
+        assert d.max() <= 2e-2 and d.mean() <= 2e-3, (h, d.max(), d.mean())
+
+
 def test_dense_kernel_matches_oracle_bf16():
     w = synth.custom_workload(B=1, Hq=4, Hkv=2, N=1024, d=128, dtype="bf16", tile_m=128,
                               seg_len=1024, structure="stripes+band", n_stripes=10, seed=77)

@@ -28,12 +28,15 @@
 //      over the range (LDS atomics count them, a scan places them), then each
 //      entry's rank inside its sub-bucket is counted by comparing (key,
 //      position) with the few entries sharing it.  A range whose sub-buckets
-//      are too full (clustered or repeated scores) or that exceeds the LDS
-//      capacity is queued.  The queue is drained afterwards by stable 8-bit
-//      LSD passes over the bytes of the position, then of the key, that vary
-//      inside the range (both taken relative to the range's lowest value): in
-//      LDS when the range fits, else through global scratch, chunk by chunk in
-//      order.  Slower, exact, and ordered by (key, position) like the rest.
+//      are too full (clustered or repeated scores) or that exceeds the stage
+//      (RANGE_CAP entries, sized for five workgroups per CU) is queued.  The
+//      queue is drained afterwards: a range of up to CAP entries is ranked by
+//      sub-buckets again in a larger stage, else (crowded sub-buckets) by
+//      stable 8-bit LSD passes over the bytes of the position, then of the
+//      key, that vary inside the range (both relative to the range's lowest
+//      value); a larger range by the same LSD passes through global scratch,
+//      chunk by chunk in order.  Exact, and ordered by (key, position) like the
+//      rest.
 // When no list is longer than the LDS capacity (block lists, short sequences)
 // one workgroup sorts each whole list in LDS and no workspace is used.
 #include "s2o_internal.h"
@@ -50,6 +53,7 @@ constexpr int MAX_BLOCK = 4096;  // entries per pass-1 block
 constexpr int MAX_CHUNK = 2048;  // output positions owned by a range-sort workgroup
 constexpr int CAP = 4096;        // entries a range-sort workgroup holds in LDS
 constexpr int CAP_ROUNDS = CAP / THREADS;
+constexpr int RANGE_CAP = 3072;  // entries a range-sort workgroup stages (5 workgroups per CU)
 constexpr int OVERFLOW_GRID = 1024;  // workgroups draining the overflow queue
 constexpr int NSB = 1536;        // value-linear sub-buckets of a range (LDS: 4 ranges per CU)
 constexpr int SUB_LIMIT = 32;    // largest sub-bucket ranked by direct comparison
@@ -622,8 +626,8 @@ struct Overflow {
 
 // One workgroup per chunk of C output positions of a list: sorts the buckets
 // that start inside the chunk (see the file comment) and writes positions.
-// A range larger than CAP, or with a sub-bucket fuller than SUB_LIMIT, is
-// queued for overflow_kernel instead.
+// A range larger than RANGE_CAP, or with a sub-bucket fuller than SUB_LIMIT,
+// is queued for overflow_kernel instead.
 template <int C>
 __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__restrict__ pairs,
                                                                 int32_t *__restrict__ idx,
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
                                                                 Overflow *__restrict__ queue,
                                                                 int32_t *__restrict__ queue_len,
                                                                 Geometry g, int E) {
-    __shared__ u32x2 stage[CAP];
+    __shared__ u32x2 stage[RANGE_CAP];
     __shared__ int sbc[NSB + 1];
     __shared__ int sred[4 * NWAVES];
     const int tid = threadIdx.x;
@@ -646,7 +650,7 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
     const int hi_b = __syncthreads_count(bs[tid] < g0 + C);
     const int32_t rs = bs[lo_b], m = bs[hi_b] - rs;
     if (m == 0) return;
-    if (m > CAP) {
+    if (m > RANGE_CAP) {
         if (tid == 0) queue[atomicAdd(queue_len, 1)] = {lid, rs, m};
         return;
     }
@@ -661,7 +665,6 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
         S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
         S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
         S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
-        S2O_SORT_CASE(13) S2O_SORT_CASE(14) S2O_SORT_CASE(15) S2O_SORT_CASE(16)
 #undef S2O_SORT_CASE
         default: break;
     }
@@ -698,9 +701,10 @@ __global__ __launch_bounds__(THREADS, 4) void list_sort_kernel(const float *__re
 }
 
 // Queued ranges (clustered, repeated or very many scores): each workgroup
-// takes queued ranges in turn; one that fits in LDS is sorted there with
-// stable LSD passes, a larger one with stable LSD passes through global
-// scratch, CAP entries at a time in order.
+// takes queued ranges in turn; one that fits in LDS is ranked there by
+// sub-buckets, or with stable LSD passes when its sub-buckets are crowded, a
+// larger one with stable LSD passes through global scratch, CAP entries at a
+// time in order.
 __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ pairs,
                                                            u32x2 *__restrict__ scratch,
                                                            int32_t *__restrict__ idx,
@@ -712,6 +716,8 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
     __shared__ int dtot[NB];
     __shared__ int run[NB];
     __shared__ uint32_t red[NWAVES];
+    __shared__ int sbc[NSB + 1];
+    __shared__ int sred[4 * NWAVES];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nq = *queue_len;
     uint32_t rel[CAP_ROUNDS], key[CAP_ROUNDS];
@@ -721,12 +727,17 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
         const Overflow ov = queue[q];
         const int64_t base = list_ref(g, ov.lid).off + ov.rs;
         const int m = ov.m;
-        if (m <= CAP) {  // fits in LDS: stable LSD passes there
+        if (m <= CAP) {  // fits in LDS
             const u32x2 *in = pairs + base;
             auto load = [in](int i) { return in[i]; };
             switch ((m + THREADS - 1) / THREADS) {
 #define S2O_SORT_CASE(R) \
-    case R: sort_in_lds<R, true>(load, idx + base, m, stage, cnt, red); break;
+    case R:                                                                    \
+        if (!rank_in_sub_buckets<R>(in, idx + base, m, stage, sbc, sred)) {    \
+            __syncthreads();                                                   \
+            sort_in_lds<R, true>(load, idx + base, m, stage, cnt, red);        \
+        }                                                                      \
+        break;
                 S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
                 S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
                 S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)

@@ -192,8 +192,9 @@ def cpu_baseline(w, x, tau, exec_gpu, n_tiles):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the path shards by KV head with no communication, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer "
+              "shards by KV head with no communication, so one GPU here runs all eight KV heads)",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 

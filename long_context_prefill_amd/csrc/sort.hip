@@ -29,14 +29,14 @@
 //      entry's rank inside its sub-bucket is counted by comparing (key,
 //      position) with the few entries sharing it.  A range whose sub-buckets
 //      are too full (clustered or repeated scores) or that exceeds the stage
-//      (RANGE_CAP entries, sized for five workgroups per CU) is queued.  The
-//      queue is drained afterwards: a range of up to CAP entries is ranked by
-//      sub-buckets again in a larger stage, else (crowded sub-buckets) by
-//      stable 8-bit LSD passes over the bytes of the position, then of the
-//      key, that vary inside the range (both relative to the range's lowest
-//      value); a larger range by the same LSD passes through global scratch,
-//      chunk by chunk in order.  Exact, and ordered by (key, position) like the
-//      rest.
+//      (RANGE_CAP entries, sized for five workgroups per CU) is queued.  A
+//      second kernel ranks queued ranges of up to CAP entries by sub-buckets
+//      in a larger stage; what remains (crowded sub-buckets, or above CAP)
+//      goes to a second queue, sorted by stable 8-bit LSD passes over the
+//      bytes of the position, then of the key, that vary inside the range
+//      (both relative to the range's lowest value): in LDS when the range
+//      fits, else through global scratch, chunk by chunk in order.  Exact, and
+//      ordered by (key, position) like the rest.
 // When no list is longer than the LDS capacity (block lists, short sequences)
 // one workgroup sorts each whole list in LDS and no workspace is used.
 #include "s2o_internal.h"
@@ -54,6 +54,7 @@ constexpr int MAX_CHUNK = 2048;  // output positions owned by a range-sort workg
 constexpr int CAP = 4096;        // entries a range-sort workgroup holds in LDS
 constexpr int CAP_ROUNDS = CAP / THREADS;
 constexpr int RANGE_CAP = 3072;  // entries a range-sort workgroup stages (5 workgroups per CU)
+constexpr int QUEUED_GRID = 1024;    // workgroups ranking the queued ranges
 constexpr int OVERFLOW_GRID = 1024;  // workgroups draining the overflow queue
 constexpr int NSB = 1536;        // value-linear sub-buckets of a range (LDS: 4 ranges per CU)
 constexpr int SUB_LIMIT = 32;    // largest sub-bucket ranked by direct comparison
@@ -161,7 +162,7 @@ __device__ Buckets list_buckets(const Geometry &g, const int32_t *blk_list, cons
 // empties the overflow queue.
 __global__ __launch_bounds__(THREADS) void plan_kernel(int32_t *__restrict__ blk_list,
                                                        int32_t *__restrict__ queue_len, Geometry g, int E) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) *queue_len = 0;
+    if (blockIdx.x == 0 && threadIdx.x < 2) queue_len[threadIdx.x] = 0;  // both queues
     const ListRef L = list_ref(g, blockIdx.x);
     const int64_t b0 = L.off / E, nb = L.len / E;
     for (int64_t i = threadIdx.x; i < nb; i += THREADS) blk_list[b0 + i] = (int32_t)blockIdx.x;
@@ -700,11 +701,46 @@ __global__ __launch_bounds__(THREADS, 4) void list_sort_kernel(const float *__re
     }
 }
 
-// Queued ranges (clustered, repeated or very many scores): each workgroup
-// takes queued ranges in turn; one that fits in LDS is ranked there by
-// sub-buckets, or with stable LSD passes when its sub-buckets are crowded, a
-// larger one with stable LSD passes through global scratch, CAP entries at a
-// time in order.
+// Queued ranges of up to CAP entries, ranked by sub-buckets in a CAP-entry
+// stage (range_sort_kernel's stage is smaller); each workgroup takes queued
+// ranges in turn.  Ranges above CAP, and those whose sub-buckets are crowded,
+// go on to the second queue.
+__global__ __launch_bounds__(THREADS, 4) void queued_range_kernel(const u32x2 *__restrict__ pairs,
+                                                                  int32_t *__restrict__ idx,
+                                                                  const Overflow *__restrict__ queue,
+                                                                  const int32_t *__restrict__ queue_len,
+                                                                  Overflow *__restrict__ queue2,
+                                                                  int32_t *__restrict__ queue2_len,
+                                                                  Geometry g) {
+    __shared__ u32x2 stage[CAP];
+    __shared__ int sbc[NSB + 1];
+    __shared__ int sred[4 * NWAVES];
+    const int tid = threadIdx.x;
+    const int nq = *queue_len;
+    for (int q = blockIdx.x; q < nq; q += gridDim.x) {
+        const Overflow ov = queue[q];
+        const int64_t base = list_ref(g, ov.lid).off + ov.rs;
+        const int m = ov.m;
+        bool done = false;
+        switch ((m + THREADS - 1) / THREADS) {
+#define S2O_SORT_CASE(R) \
+    case R: done = rank_in_sub_buckets<R>(pairs + base, idx + base, m, stage, sbc, sred); break;
+            S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
+            S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
+            S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
+            S2O_SORT_CASE(13) S2O_SORT_CASE(14) S2O_SORT_CASE(15) S2O_SORT_CASE(16)
+#undef S2O_SORT_CASE
+            default: break;  // above CAP
+        }
+        if (!done && tid == 0) queue2[atomicAdd(queue2_len, 1)] = ov;
+        __syncthreads();  // the next range reuses the LDS
+    }
+}
+
+// Ranges left over by queued_range_kernel (crowded sub-buckets, or above CAP):
+// each workgroup takes them in turn; one that fits in LDS is sorted there
+// with stable LSD passes, a larger one with stable LSD passes through global
+// scratch, CAP entries at a time in order.
 __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ pairs,
                                                            u32x2 *__restrict__ scratch,
                                                            int32_t *__restrict__ idx,
@@ -716,8 +752,6 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
     __shared__ int dtot[NB];
     __shared__ int run[NB];
     __shared__ uint32_t red[NWAVES];
-    __shared__ int sbc[NSB + 1];
-    __shared__ int sred[4 * NWAVES];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nq = *queue_len;
     uint32_t rel[CAP_ROUNDS], key[CAP_ROUNDS];
@@ -732,12 +766,7 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
             auto load = [in](int i) { return in[i]; };
             switch ((m + THREADS - 1) / THREADS) {
 #define S2O_SORT_CASE(R) \
-    case R:                                                                    \
-        if (!rank_in_sub_buckets<R>(in, idx + base, m, stage, sbc, sred)) {    \
-            __syncthreads();                                                   \
-            sort_in_lds<R, true>(load, idx + base, m, stage, cnt, red);        \
-        }                                                                      \
-        break;
+    case R: sort_in_lds<R, true>(load, idx + base, m, stage, cnt, red); break;
                 S2O_SORT_CASE(1) S2O_SORT_CASE(2) S2O_SORT_CASE(3) S2O_SORT_CASE(4)
                 S2O_SORT_CASE(5) S2O_SORT_CASE(6) S2O_SORT_CASE(7) S2O_SORT_CASE(8)
                 S2O_SORT_CASE(9) S2O_SORT_CASE(10) S2O_SORT_CASE(11) S2O_SORT_CASE(12)
@@ -839,7 +868,7 @@ struct SortWs {
     u32x2 *pairs, *scratch;
     int32_t *hist, *blk_list, *bstart, *queue_len;
     float *blk_mm;
-    Overflow *queue;
+    Overflow *queue, *queue2;
     size_t bytes;
 };
 
@@ -866,7 +895,9 @@ SortWs carve(const Geometry &g, void *base) {
     off += align256((size_t)lists * (NB + 1) * 4);
     w.queue = reinterpret_cast<Overflow *>(p + off);  // at most one entry per chunk
     off += align256((size_t)(n / range_chunk(g)) * sizeof(Overflow));
-    w.queue_len = reinterpret_cast<int32_t *>(p + off);
+    w.queue2 = reinterpret_cast<Overflow *>(p + off);  // a subset of the first queue
+    off += align256((size_t)(n / range_chunk(g)) * sizeof(Overflow));
+    w.queue_len = reinterpret_cast<int32_t *>(p + off);  // [0]: first queue, [1]: second
     off += 256;
     w.bytes = off;
     return w;
@@ -887,8 +918,10 @@ hipError_t run_sort(const Geometry &g, const float *scores, int32_t *idx, const 
                        w.blk_list, w.blk_mm, w.hist, w.pairs, g);
     hipLaunchKernelGGL(range_sort_kernel<C>, dim3((unsigned)(g.list_entries / C)), dim3(THREADS), 0, stream,
                        w.pairs, idx, w.blk_list, w.bstart, w.queue, w.queue_len, g, E);
+    hipLaunchKernelGGL(queued_range_kernel, dim3(QUEUED_GRID), dim3(THREADS), 0, stream, w.pairs, idx, w.queue,
+                       w.queue_len, w.queue2, w.queue_len + 1, g);
     hipLaunchKernelGGL(overflow_kernel, dim3(OVERFLOW_GRID), dim3(THREADS), 0, stream, w.pairs, w.scratch, idx,
-                       w.queue, w.queue_len, g);
+                       w.queue2, w.queue_len + 1, g);
     return hipGetLastError();
 }
 

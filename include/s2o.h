@@ -57,7 +57,8 @@ extern "C" {
 typedef enum {
     S2O_OK = 0,
     S2O_ERR_INVALID_ARG = -1, /* null pointer, bad size or divisibility, bad tau */
-    S2O_ERR_UNSUPPORTED = -2, /* valid request with no compiled kernel, or causal = 0 for s2o_* */
+    S2O_ERR_UNSUPPORTED = -2, /* valid request with no compiled kernel, causal = 0 for s2o_*,
+                                 or sizes past the kernels' index ranges (e.g. N*d*2 >= 2^31) */
     S2O_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the *_workspace_bytes query */
     S2O_ERR_HIP = -4          /* a HIP launch failed */
 } s2o_status;

@@ -67,7 +67,9 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     g.list_per_head = L;
     g.list_entries = L * g.B * g.Hq;
     g.query_entries = g.qperm ? (int64_t)g.B * g.Hq * g.N : 0;
-    // index ranges the kernels assume
+    // index ranges the kernels assume (the attention kernel addresses one KV
+    // head's K or V, and a tile's list, with 32-bit byte offsets)
+    if ((int64_t)g.N * g.d * 2 >= (1ll << 31)) return S2O_ERR_UNSUPPORTED;
     const int64_t units = (int64_t)g.B * g.Hkv * g.T;
     if ((int64_t)g.B * g.Hq * g.T >= (1ll << 31) || ((units + 7) / 8) * 8 * g.G >= (1ll << 31))
         return S2O_ERR_UNSUPPORTED;

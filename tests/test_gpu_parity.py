@@ -357,8 +357,10 @@ def test_llama8b_128k_segment_lists_sampled():
     x = synth.make_inputs(w)
     run = GpuRun(w, x, lists="segment")
     tiles = sample_tiles(w, heads=(3, 30), n_random=8, seed=6)
-    o, ex = run.attn(1e-3)
-    assert_report(compare(run, tiles, 1e-3, o, ex, check_lists=True), "bf16")
+    for tau in (1e-3, 1.38e-3):  # 1.38e-3: about the tau bench.py settles on for these lists
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex, check_lists=(tau == 1e-3)), "bf16")
+        del o, ex
 
 
 # ------------------------------------------------ index build on crafted scores --
@@ -466,8 +468,10 @@ def test_llama8b_128k_block_lists_sampled():
     x = synth.make_inputs(w)
     run = GpuRun(w, x, lists="tile_blocks")
     tiles = sample_tiles(w, heads=(5, 22), n_random=8, seed=8)
-    o, ex = run.attn(1e-3)
-    assert_report(compare(run, tiles, 1e-3, o, ex, check_lists=True), "bf16")
+    for tau in (1e-3, 1.89e-3):  # 1.89e-3: about the tau bench.py settles on for block lists
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex, check_lists=(tau == 1e-3)), "bf16")
+        del o, ex
 
 
 # ------------------------------------------------------------------- Q_perm ---
@@ -519,5 +523,7 @@ def test_llama8b_128k_query_permutation_sampled():
     x = synth.make_inputs(w)
     run = GpuRun(w, x, lists="tile", qperm=True)
     tiles = sample_tiles(w, heads=(7, 25), n_random=8, seed=10)
-    o, ex = run.attn(1.2e-3)
-    assert_report(compare(run, tiles, 1.2e-3, o, ex, check_lists=True), "bf16")
+    for tau in (1.2e-3, 1.42e-3):  # 1.42e-3: about the tau bench.py settles on with Q_perm
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex, check_lists=(tau == 1.2e-3)), "bf16")
+        del o, ex

@@ -74,6 +74,24 @@ def refine_tau(sweep, evaluate, budget=MSE_BUDGET, steps=4):
     return lo
 
 
+def stop_fired_share(exec_tiles, N, BM, BN, S):
+    """Share of tiles with history whose early stop fired, i.e. that executed
+    fewer pass-2 chunks than their list holds (exec_tiles [B, H, T]; pass 1 of
+    tile t is ((t+1)*BM - a_t) / BN key tiles, its list a_t / BN chunks, for
+    key and for block lists alike; not defined with Q_perm, whose pass 1
+    depends on the row order)."""
+    T = N // BM
+    t = np.arange(T)
+    a = (t * BM // S) * S
+    n1 = ((t + 1) * BM - a) // BN
+    full = n1 + a // BN
+    has = a > 0
+    if not has.any():
+        return None
+    ex = np.asarray(exec_tiles).reshape(-1, T)
+    return float((ex[:, has] < full[has]).mean())
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -338,6 +356,7 @@ def main():
         "attn_speedup_vs_dense": round(dense_ms / main["attn_ms"], 3),
         "density": round(main["density"], 4), "mse_vs_dense": main["mse"],
         "rel_mse_vs_dense": main["rel_mse"],
+        "stop_fired_share": stop_fired_share(main["exec_tiles"], w.N, w.tile_m, w.tile_n, w.seg_len),
         "mfma_pct_executed_tiles": round(100.0 * main["achieved"] / BF16_MFMA_PEAK_TFLOPS, 2),
         "effective_tflops_executed_tiles": round(main["achieved"], 1),
         "dense_tflops": round(dense_tiles * flop_per_tile / (dense_ms * 1e-3) / 1e12, 1),
@@ -360,6 +379,8 @@ def main():
             "speedup_vs_dense": round(dense_ms / r["ms_per_step"], 3),
             "density": round(r["density"], 4), "mse_vs_dense": r["mse"],
             "rel_mse_vs_dense": r["rel_mse"],
+            "stop_fired_share": (None if m.endswith("qperm") else
+                                 stop_fired_share(r["exec_tiles"], w.N, w.tile_m, w.tile_n, w.seg_len)),
             "mfma_pct_executed_tiles": round(100.0 * r["achieved"] / BF16_MFMA_PEAK_TFLOPS, 2),
             "tau_sweep": r["sweep"]}
     if not args.no_ranking_study:

@@ -72,3 +72,17 @@ def test_refine_tau_without_bracket():
     assert bench.refine_tau(sweep, curve, budget=1e-6) == 1e-4
     sweep = [curve(t) for t in (1e-2, 5e-3)]  # none within budget
     assert bench.refine_tau(sweep, curve, budget=1e-6) is None
+
+
+def test_stop_fired_share_counts_tiles_short_of_their_list():
+    N, BM, BN, S = 1024, 128, 64, 256  # tiles 0,1 have no history; tile t has 2 + a_t/64 tiles in full
+    T = N // BM
+    t = np.arange(T)
+    a = (t * BM // S) * S
+    full = ((t + 1) * BM - a) // BN + a // BN
+    ex = np.tile(full, (1, 2, 1)).astype(np.int32)   # [B=1, H=2, T]
+    assert bench.stop_fired_share(ex, N, BM, BN, S) == 0.0
+    ex[0, 1, 5] -= 1                                   # one of 12 tiles with history stops early
+    assert abs(bench.stop_fired_share(ex, N, BM, BN, S) - 1 / 12) < 1e-12
+    ex[0, 0, 0] = 1                                    # tiles without history never count
+    assert abs(bench.stop_fired_share(ex, N, BM, BN, S) - 1 / 12) < 1e-12

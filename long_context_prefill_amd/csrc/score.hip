@@ -108,8 +108,20 @@ __global__ __launch_bounds__(256) void guide_kernel(const T *__restrict__ K, flo
     const int64_t a = (int64_t)s * g.S;
     const int64_t n = ((a + g.S) < g.N ? (a + g.S) : (int64_t)g.N) - a;
     const T *src = K + (bg * g.N + a) * g.d + k;
+    // the sum stays one sequential chain over the rows; only the loads run
+    // ahead, GUIDE_BATCH rows at a time (one thread per element leaves few
+    // threads, so each must keep many loads in flight)
+    constexpr int GUIDE_BATCH = 32;
     float sum = 0.0f;
-    for (int64_t j = 0; j < n; ++j) sum = sum + widen<T>(src[j * g.d]);
+    int64_t j = 0;
+    for (; j + GUIDE_BATCH <= n; j += GUIDE_BATCH) {
+        float v[GUIDE_BATCH];
+#pragma unroll
+        for (int u = 0; u < GUIDE_BATCH; ++u) v[u] = widen<T>(src[(j + u) * g.d]);
+#pragma unroll
+        for (int u = 0; u < GUIDE_BATCH; ++u) sum = sum + v[u];
+    }
+    for (; j < n; ++j) sum = sum + widen<T>(src[j * g.d]);
     guides[gid] = sum * (1.0f / (float)n);
 }
 
@@ -126,8 +138,15 @@ __global__ __launch_bounds__(256) void query_score_kernel(const T *__restrict__ 
     const int b = (int)(bh / g.Hq), h = (int)(bh % g.Hq);
     const float *gd = guides + (((int64_t)b * g.Hkv + h / g.G) * g.nseg + row / g.S) * g.d;
     const T *q = Q + gid * g.d;
+    // the row in 16-byte pieces; the fma chain is still ascending k
+    constexpr int PER = 16 / (int)sizeof(T);
     float acc = 0.0f;
-    for (int k = 0; k < g.d; ++k) acc = __builtin_fmaf(widen<T>(q[k]), gd[k], acc);
+    for (int k0 = 0; k0 < g.d; k0 += PER) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(q + k0);
+        const T *e = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) acc = __builtin_fmaf(widen<T>(e[u]), gd[k0 + u], acc);
+    }
     qscores[gid] = acc;
 }
 

@@ -46,13 +46,20 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, cons
     const int64_t bh = tile / g.T;
     const T *src = Q + bh * g.N * g.d + k;
     const int64_t row0 = (int64_t)t * g.BM, a = seg_start(g, t);
+    // one sequential chain over the rows; the loads run POOL_BATCH rows ahead
+    constexpr int POOL_BATCH = 32;
     float sum = 0.0f;
-    if (qorder) {
-        const int32_t *ord = qorder + bh * g.N + row0;
-        for (int r = 0; r < g.BM; ++r) sum = sum + widen<T>(src[(a + ord[r]) * g.d]);
-    } else {
-        for (int r = 0; r < g.BM; ++r) sum = sum + widen<T>(src[(row0 + r) * g.d]);
+    const int32_t *ord = qorder ? qorder + bh * g.N + row0 : nullptr;
+    auto row_of = [&](int r) -> int64_t { return ord ? a + ord[r] : row0 + r; };
+    int r = 0;
+    for (; r + POOL_BATCH <= g.BM; r += POOL_BATCH) {
+        float v[POOL_BATCH];
+#pragma unroll
+        for (int u = 0; u < POOL_BATCH; ++u) v[u] = widen<T>(src[row_of(r + u) * g.d]);
+#pragma unroll
+        for (int u = 0; u < POOL_BATCH; ++u) sum = sum + v[u];
     }
+    for (; r < g.BM; ++r) sum = sum + widen<T>(src[row_of(r) * g.d]);
     // stored lane-major: element k of a pooled query at (k % 16) * (d / 16) + k / 16,
     // so a lane reads its d/16 elements (16c + lane, c = 0..) as one contiguous run
     qbar[tile * g.d + (k & 15) * (g.d >> 4) + (k >> 4)] = sum * (1.0f / (float)g.BM);  // exact: BM = 2^n
@@ -88,8 +95,17 @@ __global__ __launch_bounds__(256) void pool_blocks_kernel(const T *__restrict__ 
     const int k = (int)(gid % g.d);
     const int64_t blk = gid / g.d;  // (b*Hkv + kvh)*(N/BN) + c
     const T *src = K + blk * g.BN * g.d + k;
+    constexpr int BLK_BATCH = 32;  // one sequential chain; loads run a batch ahead
     float sum = 0.0f;
-    for (int r = 0; r < g.BN; ++r) sum = sum + widen<T>(src[(int64_t)r * g.d]);
+    int r = 0;
+    for (; r + BLK_BATCH <= g.BN; r += BLK_BATCH) {
+        float v[BLK_BATCH];
+#pragma unroll
+        for (int u = 0; u < BLK_BATCH; ++u) v[u] = widen<T>(src[(int64_t)(r + u) * g.d]);
+#pragma unroll
+        for (int u = 0; u < BLK_BATCH; ++u) sum = sum + v[u];
+    }
+    for (; r < g.BN; ++r) sum = sum + widen<T>(src[(int64_t)r * g.d]);
     kbar[gid] = sum * (1.0f / (float)g.BN);
 }
 

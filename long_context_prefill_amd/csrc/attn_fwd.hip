@@ -18,11 +18,15 @@
 //     with the partner lane (lane ^ 32) instead of a cross-lane tree;
 //   * the same layout makes the probabilities directly usable as the B
 //     operand of O^T = V^T P^T, so P never leaves registers;
-//   * K/V chunks of 64 keys are staged through LDS, double-buffered, with
-//     the next chunk's rows fetched into registers while the current chunk
-//     computes.  Gathered rows are read 256 contiguous bytes per row by
-//     consecutive lanes; V is written to LDS transposed (keys innermost) so
-//     the PV operand reads are contiguous;
+//   * bf16 (attn_kernel_bf16): K/V chunks of 64 keys go straight from HBM to
+//     LDS (buffer loads with the LDS bit, 16 bytes of a gathered row per
+//     lane, two stages each, K one chunk ahead of V); V stays row-major in
+//     LDS and the PV operand is read with the transposing ds_read_b64_tr_b16;
+//     the softmax reference is fixed after a tile's first chunk, with a
+//     running-max restart when a chunk's mass overflows the check;
+//   * fp32 (attn_kernel_staged): rows are staged through registers, V is
+//     written to LDS transposed (keys innermost) so the PV operand reads are
+//     contiguous;
 //   * the stop decision is uniform per workgroup: each wave ballots whether
 //     any of its rows still gains >= tau, the waves exchange one flag each
 //     through LDS at the barrier that already separates the LDS buffers;

@@ -21,7 +21,8 @@ import sys
 def short(name: str) -> str:
     for key in ("attn_kernel", "score_kernel", "pool_blocks_kernel", "pool_kernel", "minmax_kernel",
                 "hist_kernel", "scan_kernel", "scatter_kernel", "range_sort_kernel", "list_sort_kernel",
-                "overflow_kernel", "plan_kernel", "rocclr_copyBuffer"):
+                "queued_range_kernel", "overflow_kernel", "plan_kernel", "guide_kernel",
+                "query_score_kernel", "query_sort_kernel", "segpool_kernel", "rocclr_copyBuffer"):
         if key in name:
             tail = name.split(key, 1)[1]
             if key == "attn_kernel":
@@ -29,8 +30,11 @@ def short(name: str) -> str:
                 return "s2o_attn_fwd (S2O schedule)" if s2o else "dense_attn_fwd"
             if key in ("hist_kernel", "scatter_kernel", "range_sort_kernel"):
                 return key + tail.split("(")[0] + " (s2o_build_index)"
-            if key in ("minmax_kernel", "scan_kernel", "list_sort_kernel", "overflow_kernel", "plan_kernel"):
+            if key in ("minmax_kernel", "scan_kernel", "list_sort_kernel", "queued_range_kernel",
+                       "overflow_kernel", "plan_kernel", "query_sort_kernel"):
                 return key + " (s2o_build_index)"
+            if key in ("guide_kernel", "query_score_kernel", "segpool_kernel"):
+                return key + " (s2o_score)"
             if key == "score_kernel":
                 return "score_kernel (s2o_score)"
             if key == "pool_kernel":

@@ -154,9 +154,11 @@ size_t s2o_build_index_workspace_bytes(const s2o_problem *p);
 /* Index build ([GIST] KV_perm: the resulting indices form a global logical map
  * that puts likely vertical and slash stripes first).  For every list, idx
  * receives the positions [0, history length) sorted by score descending, ties
- * broken by the lower position; -0.0 and +0.0 tie.  A segmented stable sort
- * (one bucketing pass between each list's minimum and maximum score, then a
- * radix sort of each bucket range).
+ * broken by the lower position; -0.0 and +0.0 tie.  A segmented sort: one
+ * bucketing pass between each list's minimum and maximum score, then each
+ * range of buckets is ranked exactly by (score, position) inside value
+ * sub-buckets (crowded or oversized ranges by radix passes instead).  The
+ * result is deterministic.
  *   scores: device fp32 [s2o_list_entries] (from s2o_score), 16-byte aligned.
  *   idx: device int32 [s2o_list_entries], 16-byte aligned.
  *   workspace: device, >= s2o_build_index_workspace_bytes, 256-byte aligned.

@@ -8,17 +8,14 @@
 // Scores are defined bit-exactly: qbar[k] = (fp32 sum of the BM rows in
 // ascending order) * (1/BM) (per-segment lists: fp32 sum of the segment's tile
 // means in ascending order times fl(1/tiles)), then s[j] = fma chain over
-// k = 0..d-1 starting from 0.  The work is plain fp32 ALU (2*d flops per (tile, key) pair); the
-// fixed accumulation order rules out matrix cores.
+// k = 0..d-1 starting from 0 (2*d flops per (tile, key) pair).
 //
-// Layout of the score kernel: one workgroup per (b, KV head, segment s >= 1,
-// block of 256 history keys).  Each thread holds one key row in fp32
-// registers and runs it against every (query head of the group, tile of the
-// segment) pair, four pairs at a time.  A pair's pooled query is spread over
-// the 16 lanes of each row (D/16 registers per lane) and broadcast element by
-// element with DPP row_newbcast as the fma's first operand; the next four
-// pairs load while the current four compute.  Each chain is still evaluated in
-// ascending k.
+// The chains run on the matrix cores: the fp32 MFMA with one product per
+// output (32x32x1, two blocks) rounds once per step, exactly like fmaf, so
+// issuing it for k = 0, 1, ..., d-1 gives every chain of the definition bit
+// for bit.  One workgroup per (b, KV head, segment s >= 1, block of 256
+// history keys); each lane keeps one key row in fp32 registers as its operand
+// and the pooled queries (row-major [B, Hq, tiles, d]) are staged in LDS.
 #include "s2o_internal.h"
 
 namespace s2o {
@@ -60,14 +57,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const T *__restrict__ Q, cons
         for (int u = 0; u < POOL_BATCH; ++u) sum = sum + v[u];
     }
     for (; r < g.BM; ++r) sum = sum + widen<T>(src[row_of(r) * g.d]);
-    // stored lane-major: element k of a pooled query at (k % 16) * (d / 16) + k / 16,
-    // so a lane reads its d/16 elements (16c + lane, c = 0..) as one contiguous run
-    qbar[tile * g.d + (k & 15) * (g.d >> 4) + (k >> 4)] = sum * (1.0f / (float)g.BM);  // exact: BM = 2^n
+    qbar[tile * g.d + k] = sum * (1.0f / (float)g.BM);  // exact: BM = 2^n
 }
 
 // Segment representatives (per-segment lists): mean of the segment's tile
 // means, an fp32 sum over its tiles in ascending order times fl(1/tiles).
-// Elementwise, so it works in the lane-major layout unchanged.
 __global__ __launch_bounds__(256) void segpool_kernel(const float *__restrict__ qbar,
                                                       float *__restrict__ qseg, Geometry g,
                                                       int64_t total) {
@@ -217,61 +211,42 @@ __global__ __launch_bounds__(QSORT_THREADS) void query_sort_kernel(const float *
     for (int i = threadIdx.x; i < n; i += QSORT_THREADS) dst[i] = row[i];
 }
 
-constexpr int SCORE_KEYS = 256;   // keys per workgroup (one per thread)
-constexpr int SCORE_ILP = 4;      // pairs evaluated together (independent fma chains)
+// Scores on the matrix cores.  v_mfma_f32_32x32x1_2b_f32 adds one product per
+// output per instruction with a single rounding, i.e. it is fmaf elementwise, so
+// a chain of them over k = 0..d-1 reproduces the fma chain of the definition
+// bit for bit while doing two 32x32 outer products per instruction: block b
+// takes its 32 rows from A lanes [32b, 32b+32) and its 32 columns from B lanes
+// [32b, 32b+32).  Here the rows are 32 (query head, tile) pairs (the same pairs
+// in both blocks) and the columns are keys: every lane holds its own key row
+// in fp32 registers as its B operand, so a wave scores 64 keys against NG
+// groups of 32 pairs per pass.  The pooled queries of a pass are staged in LDS
+// (row-major, padded by 4 floats against bank conflicts).
+constexpr int MS_KEYS = 256;  // keys per workgroup: 4 waves x 64
 
-// acc[p] = fma(qbar_p[16c + n], kr[16c + n], acc[p]) for n = 0..15 in ascending
-// order, for the four pairs p.  Lane i of every 16-lane row holds
-// qbar_p[16c + i] in q_p; DPP row_newbcast:n hands lane n's value to its whole
-// row, so every fma takes its pooled-query element straight from another
-// lane's register at full rate.  The four chains are interleaved, which keeps
-// three instructions between dependent ones (DPP needs two wait states after a
-// VALU write of an operand); the leading s_nop covers writes made just before.
-#define S2O_DPP_FMA(n, K)                                                                    \
-    "v_fmac_f32_dpp %0, %4, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"        \
-    "v_fmac_f32_dpp %1, %5, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"        \
-    "v_fmac_f32_dpp %2, %6, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"        \
-    "v_fmac_f32_dpp %3, %7, " K " row_newbcast:" #n " row_mask:0xf bank_mask:0xf\n\t"
-
-__device__ __forceinline__ void fma16x4(float &a0, float &a1, float &a2, float &a3, float q0, float q1,
-                                        float q2, float q3, const float *k) {
-    asm volatile("s_nop 1\n\t"
-                 S2O_DPP_FMA(0, "%8") S2O_DPP_FMA(1, "%9") S2O_DPP_FMA(2, "%10") S2O_DPP_FMA(3, "%11")
-                 S2O_DPP_FMA(4, "%12") S2O_DPP_FMA(5, "%13") S2O_DPP_FMA(6, "%14") S2O_DPP_FMA(7, "%15")
-                 S2O_DPP_FMA(8, "%16") S2O_DPP_FMA(9, "%17") S2O_DPP_FMA(10, "%18") S2O_DPP_FMA(11, "%19")
-                 S2O_DPP_FMA(12, "%20") S2O_DPP_FMA(13, "%21") S2O_DPP_FMA(14, "%22") S2O_DPP_FMA(15, "%23")
-                 : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3)
-                 : "v"(q0), "v"(q1), "v"(q2), "v"(q3), "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]),
-                   "v"(k[5]), "v"(k[6]), "v"(k[7]), "v"(k[8]), "v"(k[9]), "v"(k[10]), "v"(k[11]), "v"(k[12]),
-                   "v"(k[13]), "v"(k[14]), "v"(k[15])
-                 : "memory");  // keeps the next group's loads issued ahead of the block
-}
-#undef S2O_DPP_FMA
-
-template <typename T, int D>
-__global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__restrict__ qbar,
-                                                              const T *__restrict__ K,
-                                                              float *__restrict__ scores,
-                                                              Geometry g, int nseg) {
-    constexpr int NQ = D / 16;                   // 16-element chunks of a pooled query
-    const int s = blockIdx.y % nseg;             // segment of the query tiles
-    const int bg = blockIdx.y / nseg;            // b * Hkv + kv head
-    const int hist = s * g.S;                    // history length of the segment's tiles
-    const int j0 = blockIdx.x * SCORE_KEYS;
-    if (s == 0 || j0 >= hist) return;
+template <typename T, int D, int NG>
+__global__ __launch_bounds__(MS_KEYS, 2) void score_mfma_kernel(const float *__restrict__ qbar,
+                                                               const T *__restrict__ K,
+                                                               float *__restrict__ scores, Geometry g,
+                                                               int nseg) {
+    typedef float f32x32 __attribute__((ext_vector_type(32)));
+    constexpr int ROWS = 32 * NG, PITCH = D + 4;
+    __shared__ __attribute__((aligned(16))) float qs[ROWS * PITCH];
+    const int s = blockIdx.y % nseg;
+    const int bg = blockIdx.y / nseg;
+    const int hist = s * g.S;
+    if (s == 0 || (int)blockIdx.x * MS_KEYS >= hist) return;  // uniform
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int b = bg / g.Hkv, kvh = bg % g.Hkv;
     const int t_first = s * g.P;
-    // per-tile lists: one pair per (query head, tile of the segment); per-segment
-    // lists: one pair per query head, ranked against the segment representative
     const int ntiles = g.per_seg ? 1 : min(g.T, (s + 1) * g.P) - t_first;
-    const int npairs = ntiles * g.G;             // pair p -> (query head kvh*G + p / ntiles, tile)
-    const int j = j0 + (int)threadIdx.x;
-    const bool live = j < hist;
-    const int col = threadIdx.x & 15;            // this lane's element of each 16-chunk
+    const int npairs = ntiles * g.G;
+    const int j0 = blockIdx.x * MS_KEYS + wave * 64;  // this wave's keys
+    const bool wave_live = j0 < hist;                 // uniform per wave
+    const int j = j0 + lane;
 
     float kr[D];
     {
-        const T *row = K + ((int64_t)bg * g.N + (live ? j : 0)) * D;
+        const T *row = K + ((int64_t)bg * g.N + (j < hist ? j : 0)) * D;
 #pragma unroll
         for (int k = 0; k < D; k += 8) {
             uint4 raw = *reinterpret_cast<const uint4 *>(row + k);  // 8 bf16 or 4 fp32
@@ -298,83 +273,85 @@ __global__ __launch_bounds__(SCORE_KEYS, 2) void score_kernel(const float *__res
 
     // Pair pp -> (query head kvh*G + hq, tile t_first + ti), hq = pp / ntiles by a
     // multiply-high with ceil(2^32 / ntiles) (exact while pp * ntiles < 2^32,
-    // else a plain division), and
-    // the pair's pooled query and list position in closed form (the tiles of
-    // one head are consecutive in both layouts; the list of tile t_first + ti
-    // starts ti * S * s after the segment's first list).
+    // else a plain division), and the pair's pooled query and list position in
+    // closed form (the tiles of one head are consecutive in both layouts; the
+    // list of tile t_first + ti starts ti * S * s after the segment's first list).
     const uint32_t magic = ntiles > 1 ? (uint32_t)((0x100000000ull + ntiles - 1) / (uint64_t)ntiles) : 0u;
     const bool by_magic = (int64_t)npairs * ntiles < 0x100000000ll;
+    auto split = [&](int pp, int &hq, int &ti) {
+        hq = ntiles == 1 ? pp : by_magic ? (int)__umulhi((uint32_t)pp, magic) : pp / ntiles;
+        ti = pp - hq * ntiles;
+    };
     const int qrows = g.per_seg ? g.nseg : g.T;  // pooled queries per head
     const float *qhead0 = qbar + (((int64_t)b * g.Hq + kvh * g.G) * qrows + (g.per_seg ? s : t_first)) * D;
     const int64_t L = g.list_per_head;
     const int64_t seg_first = g.per_seg ? (int64_t)g.S * (s * (s - 1) / 2)
                                         : (int64_t)g.S * ((int64_t)g.P * s * (s - 1) / 2);
-    float *shead0 = scores + ((int64_t)b * g.Hq + kvh * g.G) * L + seg_first + j;
+    float *shead0 = scores + ((int64_t)b * g.Hq + kvh * g.G) * L + seg_first;
     const int64_t tile_step = g.per_seg ? 0 : (int64_t)g.S * s;
-    auto split = [&](int pp, int &hq, int &ti) {
-        hq = ntiles == 1 ? pp : by_magic ? (int)__umulhi((uint32_t)pp, magic) : pp / ntiles;
-        ti = pp - hq * ntiles;
-    };
-    // q[i][c] = pooled query of pair p0 + i, element 16c + col (every row alike),
-    // read as NQ contiguous floats of the lane-major layout
-    auto load_group = [&](float (&q)[SCORE_ILP][NQ], int p0) {
-#pragma unroll
-        for (int i = 0; i < SCORE_ILP; ++i) {
-            int hq, ti;
-            split(min(p0 + i, npairs - 1), hq, ti);
-            const float *src = qhead0 + ((int64_t)hq * qrows + ti) * D + col * NQ;
-#pragma unroll
-            for (int c = 0; c < NQ; c += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(src + c);
-                q[i][c] = v.x;
-                q[i][c + 1] = v.y;
-                q[i][c + 2] = v.z;
-                q[i][c + 3] = v.w;
-            }
-        }
-    };
-    auto store_group = [&](const float (&acc)[SCORE_ILP], int p0) {
-#pragma unroll
-        for (int i = 0; i < SCORE_ILP; ++i) {
-            if (live && p0 + i < npairs) {
-                int hq, ti;
-                split(p0 + i, hq, ti);
-                shead0[hq * L + ti * tile_step] = acc[i];
-            }
-        }
-    };
-    // Runs the four chains of pairs p0..p0+3 on q.  The previous group's scores
-    // and the next group's loads go out after the first 16 steps, so that when
-    // the next group starts, every memory operation it waits for (loads and
-    // stores share one counter) was issued a whole group earlier.
-    auto run_group = [&](const float (&q)[SCORE_ILP][NQ], int p0, float (&qnext)[SCORE_ILP][NQ],
-                         float (&acc)[SCORE_ILP]) {
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        fma16x4(a0, a1, a2, a3, q[0][0], q[1][0], q[2][0], q[3][0], kr);
-        if (p0 > 0) store_group(acc, p0 - SCORE_ILP);
-        if (p0 + SCORE_ILP < npairs) load_group(qnext, p0 + SCORE_ILP);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 1; c < NQ; ++c)
-            fma16x4(a0, a1, a2, a3, q[0][c], q[1][c], q[2][c], q[3][c], kr + 16 * c);
-        acc[0] = a0;
-        acc[1] = a1;
-        acc[2] = a2;
-        acc[3] = a3;
-    };
 
-    float qa[SCORE_ILP][NQ], qb[SCORE_ILP][NQ], acc[SCORE_ILP];
-    load_group(qa, 0);
-    int p0 = 0;
-    for (;;) {
-        run_group(qa, p0, qb, acc);
-        if (p0 + SCORE_ILP >= npairs) break;
-        p0 += SCORE_ILP;
-        run_group(qb, p0, qa, acc);
-        if (p0 + SCORE_ILP >= npairs) break;
-        p0 += SCORE_ILP;
+    for (int p0 = 0; p0 < npairs; p0 += ROWS) {
+        // stage the pooled queries of pairs p0 .. p0+ROWS-1 (zeros past the last)
+        constexpr int C4 = D / 4;
+        for (int i = tid; i < ROWS * C4; i += MS_KEYS) {
+            const int r = i / C4, c4 = i % C4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (p0 + r < npairs) {
+                int hq, ti;
+                split(p0 + r, hq, ti);
+                v = *reinterpret_cast<const float4 *>(qhead0 + ((int64_t)hq * qrows + ti) * D + 4 * c4);
+            }
+            *reinterpret_cast<float4 *>(&qs[r * PITCH + 4 * c4]) = v;
+        }
+        __syncthreads();
+        if (wave_live) {
+            f32x32 acc[NG];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int r = 0; r < 32; ++r) acc[gi][r] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < D; kk += 4) {
+                float4 a[NG];
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi)
+                    a[gi] = *reinterpret_cast<const float4 *>(&qs[(32 * gi + (lane & 31)) * PITCH + kk]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi)
+                        acc[gi] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[gi][u], kr[kk + u], acc[gi], 0, 0, 0);
+            }
+            // acc[gi][16*blk + rr] = score of pair p0 + 32 gi + 8 (rr/4) + 4 (lane/32) + rr%4
+            // against key j0 + 32 blk + lane%32
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+                for (int r = 0; r < 32; ++r) {
+                    const int blk = r >> 4, rr = r & 15;
+                    const int pp = p0 + 32 * gi + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+                    const int key = j0 + 32 * blk + (lane & 31);
+                    if (pp < npairs && key < hist) {
+                        int hq, ti;
+                        split(pp, hq, ti);
+                        shead0[hq * L + ti * tile_step + key] = acc[gi][r];
+                    }
+                }
+            }
+        }
+        __syncthreads();  // the next pass restages qs
     }
-    store_group(acc, p0);
+}
+
+template <typename T, int D>
+void launch_score_mfma(bool two_groups, dim3 grid, const float *qbar, const void *K, float *scores,
+                       const Geometry &g, int nseg, hipStream_t stream) {
+    if (two_groups)
+        hipLaunchKernelGGL((score_mfma_kernel<T, D, 2>), grid, dim3(MS_KEYS), 0, stream, qbar,
+                           reinterpret_cast<const T *>(K), scores, g, nseg);
+    else
+        hipLaunchKernelGGL((score_mfma_kernel<T, D, 1>), grid, dim3(MS_KEYS), 0, stream, qbar,
+                           reinterpret_cast<const T *>(K), scores, g, nseg);
 }
 
 }  // namespace
@@ -438,21 +415,14 @@ hipError_t launch_score(const Geometry &g, const float *qbar, const void *K, flo
     const int nseg = (g.N + g.S - 1) / g.S;
     if (nseg < 2) return hipSuccess;  // no tile has history
     const int64_t max_hist = (int64_t)(nseg - 1) * g.S;
-    dim3 grid((unsigned)((max_hist + SCORE_KEYS - 1) / SCORE_KEYS), (unsigned)(g.B * g.Hkv * nseg));
+    dim3 grid((unsigned)((max_hist + MS_KEYS - 1) / MS_KEYS), (unsigned)(g.B * g.Hkv * nseg));
+    const bool two = (g.per_seg ? 1 : g.P) * g.G > 32;  // pairs per segment
     if (g.dtype == 1) {
-        if (g.d == 128)
-            hipLaunchKernelGGL((score_kernel<__bf16, 128>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
-                               reinterpret_cast<const __bf16 *>(K), scores, g, nseg);
-        else
-            hipLaunchKernelGGL((score_kernel<__bf16, 64>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
-                               reinterpret_cast<const __bf16 *>(K), scores, g, nseg);
+        if (g.d == 128) launch_score_mfma<__bf16, 128>(two, grid, qbar, K, scores, g, nseg, stream);
+        else launch_score_mfma<__bf16, 64>(two, grid, qbar, K, scores, g, nseg, stream);
     } else {
-        if (g.d == 128)
-            hipLaunchKernelGGL((score_kernel<float, 128>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
-                               reinterpret_cast<const float *>(K), scores, g, nseg);
-        else
-            hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(SCORE_KEYS), 0, stream, qbar,
-                               reinterpret_cast<const float *>(K), scores, g, nseg);
+        if (g.d == 128) launch_score_mfma<float, 128>(two, grid, qbar, K, scores, g, nseg, stream);
+        else launch_score_mfma<float, 64>(two, grid, qbar, K, scores, g, nseg, stream);
     }
     return hipGetLastError();
 }

@@ -18,29 +18,30 @@ import json
 import sys
 
 
+KERNELS = {  # kernel name -> the entry point that launches it
+    "attn_kernel": None, "score_mfma_kernel": "s2o_score", "pool_kernel": "s2o_score",
+    "segpool_kernel": "s2o_score", "pool_blocks_kernel": "s2o_score", "guide_kernel": "s2o_score",
+    "query_score_kernel": "s2o_score", "minmax_kernel": "s2o_build_index",
+    "hist_kernel": "s2o_build_index", "scan_kernel": "s2o_build_index",
+    "scatter_kernel": "s2o_build_index", "range_sort_kernel": "s2o_build_index",
+    "list_sort_kernel": "s2o_build_index", "queued_range_kernel": "s2o_build_index",
+    "overflow_kernel": "s2o_build_index", "plan_kernel": "s2o_build_index",
+    "query_sort_kernel": "s2o_build_index", "rocclr_copyBuffer": None,
+}
+
+
 def short(name: str) -> str:
-    for key in ("attn_kernel", "score_kernel", "pool_blocks_kernel", "pool_kernel", "minmax_kernel",
-                "hist_kernel", "scan_kernel", "scatter_kernel", "range_sort_kernel", "list_sort_kernel",
-                "queued_range_kernel", "overflow_kernel", "plan_kernel", "guide_kernel",
-                "query_score_kernel", "query_sort_kernel", "segpool_kernel", "rocclr_copyBuffer"):
-        if key in name:
-            tail = name.split(key, 1)[1]
-            if key == "attn_kernel":
-                s2o = "ELb1E" in tail or ", true>" in tail
-                return "s2o_attn_fwd (S2O schedule)" if s2o else "dense_attn_fwd"
-            if key in ("hist_kernel", "scatter_kernel", "range_sort_kernel"):
-                return key + tail.split("(")[0] + " (s2o_build_index)"
-            if key in ("minmax_kernel", "scan_kernel", "list_sort_kernel", "queued_range_kernel",
-                       "overflow_kernel", "plan_kernel", "query_sort_kernel"):
-                return key + " (s2o_build_index)"
-            if key in ("guide_kernel", "query_score_kernel", "segpool_kernel"):
-                return key + " (s2o_score)"
-            if key == "score_kernel":
-                return "score_kernel (s2o_score)"
-            if key == "pool_kernel":
-                return "pool_kernel (s2o_score)"
-            return key
-    return name[:60]
+    # the longest key wins: several kernel names contain a shorter one
+    hits = [k for k in KERNELS if k in name]
+    if not hits:
+        return name[:60]
+    key = max(hits, key=len)
+    tail = name.split(key, 1)[1]
+    if key == "attn_kernel":
+        s2o = "ELb1E" in tail or ", true>" in tail
+        return "s2o_attn_fwd (S2O schedule)" if s2o else "dense_attn_fwd"
+    label = key + tail.split("(")[0] if key in ("hist_kernel", "scatter_kernel", "range_sort_kernel") else key
+    return f"{label} ({KERNELS[key]})" if KERNELS[key] else key
 
 
 def per_kernel(path, value="Counter_Value"):

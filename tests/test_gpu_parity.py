@@ -59,6 +59,23 @@ def test_tiny_f32_segments_512(tau):
     assert_report(rep, "f32")
 
 
+@pytest.mark.parametrize("q_exp,k_exp", [(-75, -65), (-132, 0)], ids=["denormal_products", "denormal_inputs"])
+def test_tiny_f32_denormal_scores_bit_exact(q_exp, k_exp):
+    """Inputs scaled so that the fma products (or the pooled queries themselves)
+    fall below 2^-126: the scores keep every denormal bit of the oracle's fmaf
+    chain, and the lists (rich in ties at that precision) match."""
+    w = synth.WORKLOADS["tiny_f32_n2048_s512"]
+    x = dict(synth.make_inputs(w))
+    x["q"] = (x["q"] * np.float32(2.0 ** q_exp)).astype(np.float32)
+    x["k"] = (x["k"] * np.float32(2.0 ** k_exp)).astype(np.float32)
+    run = GpuRun(w, x)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    sub = np.abs(scores_o) < np.float32(2.0 ** -126)
+    assert sub.mean() > 0.9 and np.count_nonzero(scores_o) > 0.9 * scores_o.size
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+
+
 # ------------------------------------------------------- small bf16, every tile --
 
 SMALL = [

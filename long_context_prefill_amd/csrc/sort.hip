@@ -75,15 +75,19 @@ __device__ inline uint32_t desc_key(float f) {
 
 __device__ inline uint64_t lanemask_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
 
-// Lanes of the wave holding the same 8-bit digit as this lane.
+// Lanes of the wave holding the same 8-bit digit as this lane: per bit, the
+// ballot of lanes with the bit set, complemented where this lane's bit is
+// clear (xnor with the bit spread over a word), ANDed over the bits.
 __device__ inline uint64_t match_digit(uint32_t digit) {
-    uint64_t peers = ~0ull;
+    uint32_t lo = ~0u, hi = ~0u;
 #pragma unroll
     for (int bit = 0; bit < 8; ++bit) {
-        uint64_t bal = __ballot((digit >> bit) & 1u);
-        peers &= ((digit >> bit) & 1u) ? bal : ~bal;
+        const uint32_t m = (uint32_t)((int32_t)(digit << (31 - bit)) >> 31);  // 0 or ~0
+        const uint64_t bal = __ballot(m != 0u);
+        lo &= ~((uint32_t)bal ^ m);
+        hi &= ~((uint32_t)(bal >> 32) ^ m);
     }
-    return peers;
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Exclusive scan of 256 ints in LDS, in place, by the first wave; the totals'

@@ -231,6 +231,7 @@ __global__ __launch_bounds__(MS_KEYS, 2) void score_mfma_kernel(const float *__r
     typedef float f32x32 __attribute__((ext_vector_type(32)));
     constexpr int ROWS = 32 * NG, PITCH = D + 4;
     __shared__ __attribute__((aligned(16))) float qs[ROWS * PITCH];
+    __shared__ __attribute__((aligned(16))) int64_t srow[ROWS];  // list start of each staged pair, or -1
     const int s = blockIdx.y % nseg;
     const int bg = blockIdx.y / nseg;
     const int hist = s * g.S;
@@ -303,6 +304,15 @@ __global__ __launch_bounds__(MS_KEYS, 2) void score_mfma_kernel(const float *__r
             }
             *reinterpret_cast<float4 *>(&qs[r * PITCH + 4 * c4]) = v;
         }
+        for (int r = tid; r < ROWS; r += MS_KEYS) {
+            int64_t o = -1;
+            if (p0 + r < npairs) {
+                int hq, ti;
+                split(p0 + r, hq, ti);
+                o = hq * L + ti * tile_step;
+            }
+            srow[r] = o;
+        }
         __syncthreads();
         if (wave_live) {
             f32x32 acc[NG];
@@ -322,20 +332,25 @@ __global__ __launch_bounds__(MS_KEYS, 2) void score_mfma_kernel(const float *__r
                     for (int gi = 0; gi < NG; ++gi)
                         acc[gi] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[gi][u], kr[kk + u], acc[gi], 0, 0, 0);
             }
-            // acc[gi][16*blk + rr] = score of pair p0 + 32 gi + 8 (rr/4) + 4 (lane/32) + rr%4
-            // against key j0 + 32 blk + lane%32
+            // acc[gi][16*blk + 4*q + e] = score of staged pair 32 gi + 8 q + 4 (lane/32) + e
+            // against key j0 + 32 blk + lane%32; a pair's list start comes from srow
+            const bool full = p0 + ROWS <= npairs && j0 + 64 <= hist;  // uniform per wave
+            const int kl = j0 + (lane & 31);
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
-                for (int r = 0; r < 32; ++r) {
-                    const int blk = r >> 4, rr = r & 15;
-                    const int pp = p0 + 32 * gi + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-                    const int key = j0 + 32 * blk + (lane & 31);
-                    if (pp < npairs && key < hist) {
-                        int hq, ti;
-                        split(pp, hq, ti);
-                        shead0[hq * L + ti * tile_step + key] = acc[gi][r];
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    int64_t ro[4];
+                    const int rb = 32 * gi + 8 * q + 4 * (lane >> 5);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ro[e] = srow[rb + e];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int blk = 0; blk < 2; ++blk) {
+                            const int key = kl + 32 * blk;
+                            if (full || (ro[e] >= 0 && key < hist)) shead0[ro[e] + key] = acc[gi][16 * blk + 4 * q + e];
+                        }
                 }
             }
         }

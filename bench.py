@@ -132,6 +132,20 @@ def traffic_figure():
     return rec.get("hbm_bytes_per_launch")
 
 
+def gather_figure(attn_ms):
+    """Bytes the attention kernel moves beyond L2 per launch (the committed
+    FETCH_SIZE + WRITE_SIZE profile of this kernel source) over its live
+    average duration, against the HBM peak; None without a matching profile.
+    The counters include requests that the Infinity Cache serves."""
+    t = traffic_figure()
+    if t is None:
+        return None
+    gbs = t / (attn_ms * 1e-3) / 1e9
+    return {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": t,
+            "counts": "FETCH_SIZE + WRITE_SIZE beyond L2, Infinity Cache hits included"}
+
+
 def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles, rows_of=None):
     """How well a tile's list order matches each row's true attention order.
 
@@ -366,6 +380,7 @@ def main():
                      "frac": round(main["achieved"] / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_figure(), "kernel": "s2o_attn_fwd",
                      "work": f"{main['executed']} executed 128x64 tiles x {flop_per_tile:.0f} flop"},
+        "gathers": gather_figure(main["attn_ms"]),
     }
     names = {"segment": "segment_lists", "tile_blocks": "block_lists",
              "segment_blocks": "segment_block_lists", "tile+qperm": "query_permutation",

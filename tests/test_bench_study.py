@@ -86,3 +86,16 @@ def test_stop_fired_share_counts_tiles_short_of_their_list():
     assert abs(bench.stop_fired_share(ex, N, BM, BN, S) - 1 / 12) < 1e-12
     ex[0, 0, 0] = 1                                    # tiles without history never count
     assert abs(bench.stop_fired_share(ex, N, BM, BN, S) - 1 / 12) < 1e-12
+
+
+def test_gather_figure_matches_committed_profile():
+    """The gather bandwidth is the committed profile's bytes over the given time,
+    and absent when the profile does not match the kernel source."""
+    t = bench.traffic_figure()
+    g = bench.gather_figure(100.0)
+    if t is None:
+        assert g is None
+        return
+    assert g["unit"] == "GB/s" and g["peak"] == bench.HBM_PEAK_GBS
+    assert abs(g["achieved"] - t / 0.1 / 1e9) < 0.1
+    assert abs(g["frac"] - g["achieved"] / bench.HBM_PEAK_GBS) < 1e-3

@@ -221,15 +221,23 @@ __global__ __launch_bounds__(QSORT_THREADS) void query_sort_kernel(const float *
 // in fp32 registers as its B operand, so a wave scores 64 keys against NG
 // groups of 32 pairs per pass.  The pooled queries of a pass are staged in LDS
 // (row-major, padded by 4 floats against bank conflicts).
+// Segments with few pairs (per-segment lists have one pair per query head)
+// use v_mfma_f32_4x4x1_16b_f32 instead (SHAPE 4), which rounds the same way:
+// its 16 blocks take their 4 rows from A lanes 4b..4b+3 and column j from B
+// lane j, so with lane l holding the pooled query of pair l%4 as A one
+// instruction scores 4 pairs against the wave's 64 keys, and output register r
+// of lane l is pair r against the lane's own key.
 constexpr int MS_KEYS = 256;  // keys per workgroup: 4 waves x 64
 
-template <typename T, int D, int NG>
+template <typename T, int D, int SHAPE, int NG>
 __global__ __launch_bounds__(MS_KEYS, 2) void score_mfma_kernel(const float *__restrict__ qbar,
                                                                const T *__restrict__ K,
                                                                float *__restrict__ scores, Geometry g,
                                                                int nseg) {
+    static_assert(SHAPE == 32 || SHAPE == 4, "32x32x1 or 4x4x1 blocks");
     typedef float f32x32 __attribute__((ext_vector_type(32)));
-    constexpr int ROWS = 32 * NG, PITCH = D + 4;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int ROWS = SHAPE * NG, PITCH = D + 4;
     __shared__ __attribute__((aligned(16))) float qs[ROWS * PITCH];
     __shared__ __attribute__((aligned(16))) int64_t srow[ROWS];  // list start of each staged pair, or -1
     const int s = blockIdx.y % nseg;
@@ -314,7 +322,33 @@ __global__ __launch_bounds__(MS_KEYS, 2) void score_mfma_kernel(const float *__r
             srow[r] = o;
         }
         __syncthreads();
-        if (wave_live) {
+        if (SHAPE == 4 && wave_live) {
+            f32x4 acc[NG];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) acc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D; kk += 4) {
+                float4 a[NG];
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi)
+                    a[gi] = *reinterpret_cast<const float4 *>(&qs[(4 * gi + (lane & 3)) * PITCH + kk]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi)
+                        acc[gi] = __builtin_amdgcn_mfma_f32_4x4x1f32(a[gi][u], kr[kk + u], acc[gi], 0, 0, 0);
+            }
+            // acc[gi][r] = score of staged pair 4 gi + r against key j0 + lane
+            const int key = j0 + lane;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t o = srow[4 * gi + r];
+                    if (o >= 0 && key < hist) shead0[o + key] = acc[gi][r];
+                }
+        }
+        if (SHAPE == 32 && wave_live) {
             f32x32 acc[NG];
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi)
@@ -358,15 +392,19 @@ __global__ __launch_bounds__(MS_KEYS, 2) void score_mfma_kernel(const float *__r
     }
 }
 
+// pairs: (query head, tile) pairs of a segment
 template <typename T, int D>
-void launch_score_mfma(bool two_groups, dim3 grid, const float *qbar, const void *K, float *scores,
+void launch_score_mfma(int pairs, dim3 grid, const float *qbar, const void *K, float *scores,
                        const Geometry &g, int nseg, hipStream_t stream) {
-    if (two_groups)
-        hipLaunchKernelGGL((score_mfma_kernel<T, D, 2>), grid, dim3(MS_KEYS), 0, stream, qbar,
-                           reinterpret_cast<const T *>(K), scores, g, nseg);
+    const T *k = reinterpret_cast<const T *>(K);
+    if (pairs <= 4)
+        hipLaunchKernelGGL((score_mfma_kernel<T, D, 4, 1>), grid, dim3(MS_KEYS), 0, stream, qbar, k, scores, g, nseg);
+    else if (pairs <= 16)
+        hipLaunchKernelGGL((score_mfma_kernel<T, D, 4, 4>), grid, dim3(MS_KEYS), 0, stream, qbar, k, scores, g, nseg);
+    else if (pairs <= 32)
+        hipLaunchKernelGGL((score_mfma_kernel<T, D, 32, 1>), grid, dim3(MS_KEYS), 0, stream, qbar, k, scores, g, nseg);
     else
-        hipLaunchKernelGGL((score_mfma_kernel<T, D, 1>), grid, dim3(MS_KEYS), 0, stream, qbar,
-                           reinterpret_cast<const T *>(K), scores, g, nseg);
+        hipLaunchKernelGGL((score_mfma_kernel<T, D, 32, 2>), grid, dim3(MS_KEYS), 0, stream, qbar, k, scores, g, nseg);
 }
 
 }  // namespace
@@ -431,13 +469,13 @@ hipError_t launch_score(const Geometry &g, const float *qbar, const void *K, flo
     if (nseg < 2) return hipSuccess;  // no tile has history
     const int64_t max_hist = (int64_t)(nseg - 1) * g.S;
     dim3 grid((unsigned)((max_hist + MS_KEYS - 1) / MS_KEYS), (unsigned)(g.B * g.Hkv * nseg));
-    const bool two = (g.per_seg ? 1 : g.P) * g.G > 32;  // pairs per segment
+    const int pairs = (g.per_seg ? 1 : g.P) * g.G;  // most pairs of a segment
     if (g.dtype == 1) {
-        if (g.d == 128) launch_score_mfma<__bf16, 128>(two, grid, qbar, K, scores, g, nseg, stream);
-        else launch_score_mfma<__bf16, 64>(two, grid, qbar, K, scores, g, nseg, stream);
+        if (g.d == 128) launch_score_mfma<__bf16, 128>(pairs, grid, qbar, K, scores, g, nseg, stream);
+        else launch_score_mfma<__bf16, 64>(pairs, grid, qbar, K, scores, g, nseg, stream);
     } else {
-        if (g.d == 128) launch_score_mfma<float, 128>(two, grid, qbar, K, scores, g, nseg, stream);
-        else launch_score_mfma<float, 64>(two, grid, qbar, K, scores, g, nseg, stream);
+        if (g.d == 128) launch_score_mfma<float, 128>(pairs, grid, qbar, K, scores, g, nseg, stream);
+        else launch_score_mfma<float, 64>(pairs, grid, qbar, K, scores, g, nseg, stream);
     }
     return hipGetLastError();
 }

@@ -313,6 +313,9 @@ def main():
         ms_per_step = start.elapsed_time(end) / steps
         ph = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])
         score_ms, sort_ms, attn_ms = (float(np.mean(ph[:, j])) for j in range(3))
+        step = np.array([e[0].elapsed_time(e[3]) for e in ev])
+        step_stats = {"median": round(float(np.median(step)), 3), "min": round(float(step.min()), 3),
+                      "p90": round(float(np.percentile(step, 90)), 3)}
         executed = int(exec_tiles.sum())
         achieved = executed * flop_per_tile / (attn_ms * 1e-3) / 1e12
         study = None
@@ -330,7 +333,7 @@ def main():
         log(f"[{mode}] step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index "
             f"{sort_ms:.2f} + attn {attn_ms:.2f}")
         res = {"tau": tau, "ms_per_step": ms_per_step, "score_ms": score_ms, "sort_ms": sort_ms,
-               "attn_ms": attn_ms, "executed": executed, "density": executed / dense_tiles,
+               "attn_ms": attn_ms, "step_stats": step_stats, "executed": executed, "density": executed / dense_tiles,
                "mse": chosen["mse"], "rel_mse": chosen["rel_mse"], "achieved": achieved,
                "sweep": sweep, "exec_tiles": exec_tiles.cpu().numpy(), "study": study}
         del scores, idx, ws_score, ws_sort, out, exec_tiles
@@ -366,6 +369,7 @@ def main():
                       "s2o_build_index": round(main["sort_ms"], 3),
                       "s2o_attn_fwd": round(main["attn_ms"], 3)},
         "dense_attn_fwd_ms": round(dense_ms, 3),
+        "step_ms": main["step_stats"],
         "speedup_vs_dense": round(dense_ms / main["ms_per_step"], 3),
         "attn_speedup_vs_dense": round(dense_ms / main["attn_ms"], 3),
         "density": round(main["density"], 4), "mse_vs_dense": main["mse"],

@@ -132,6 +132,23 @@ def traffic_figure():
     return rec.get("hbm_bytes_per_launch")
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_attn_fwd_llama8b_n128k.json")
+
+
+def mfma_busy_counter():
+    """Share of SIMD cycles the matrix cores were busy in the S2O attention
+    kernel (SQ_VALU_MFMA_BUSY_CYCLES over SQ_BUSY_CYCLES scaled to SIMDs), from
+    the committed counter profile of this kernel source; None otherwise."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    k = rec.get("kernels", {}).get("s2o_attn_fwd (S2O schedule)")
+    return round(k["mfma_busy"], 4) if k else None
+
+
 def gather_figure(attn_ms):
     """Bytes the attention kernel moves beyond L2 per launch (the committed
     FETCH_SIZE + WRITE_SIZE profile of this kernel source) over its live
@@ -376,6 +393,7 @@ def main():
         "rel_mse_vs_dense": main["rel_mse"],
         "stop_fired_share": stop_fired_share(main["exec_tiles"], w.N, w.tile_m, w.tile_n, w.seg_len),
         "mfma_pct_executed_tiles": round(100.0 * main["achieved"] / BF16_MFMA_PEAK_TFLOPS, 2),
+        "mfma_busy_counter": mfma_busy_counter(),
         "effective_tflops_executed_tiles": round(main["achieved"], 1),
         "dense_tflops": round(dense_tiles * flop_per_tile / (dense_ms * 1e-3) / 1e12, 1),
         "tau_sweep": main["sweep"],

@@ -14,6 +14,7 @@ from __future__ import annotations
 import argparse
 import collections
 import csv
+import hashlib
 import json
 import sys
 
@@ -100,6 +101,11 @@ def main_counters(a):
               f"{100 * r['wave_waiting_counters_barrier']:.0f} %")
         print(f"  per MFMA: {r['valu_insts_per_mfma']:.2f} other VALU ({r['trans_per_mfma']:.2f} "
               f"transcendental), {r['lds_insts_per_mfma']:.2f} LDS instructions\n")
+    if a.json_out:
+        src = hashlib.sha256(open(a.source, "rb").read()).hexdigest()[:16] if a.source else None
+        out = {n: {k: v for k, v in r.items() if k != "counters"} for n, r in rep.items()}
+        json.dump({"kernels": out, "command": a.command, "kernel_source_sha256_16": src},
+                  open(a.json_out, "w"), indent=1)
 
 
 def main():
@@ -107,6 +113,8 @@ def main():
         ap = argparse.ArgumentParser()
         ap.add_argument("--counters", nargs="+", required=True)
         ap.add_argument("--command", required=True)
+        ap.add_argument("--json-out", help="also write the derived shares as JSON")
+        ap.add_argument("--source", help="kernel source whose hash the JSON records")
         main_counters(ap.parse_args())
         return
     ap = argparse.ArgumentParser()

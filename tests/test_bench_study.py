@@ -99,3 +99,20 @@ def test_gather_figure_matches_committed_profile():
     assert g["unit"] == "GB/s" and g["peak"] == bench.HBM_PEAK_GBS
     assert abs(g["achieved"] - t / 0.1 / 1e9) < 0.1
     assert abs(g["frac"] - g["achieved"] / bench.HBM_PEAK_GBS) < 1e-3
+
+
+def test_mfma_busy_counter_reads_the_matching_profile():
+    """The counter-based matrix-core share comes from the committed profile only
+    when that profile was taken on the current attention source."""
+    import json
+    v = bench.mfma_busy_counter()
+    try:
+        rec = json.load(open(bench.COUNTERS_FILE))
+    except OSError:
+        assert v is None
+        return
+    if rec.get("kernel_source_sha256_16") != bench.source_hash(bench.ATTN_SOURCE):
+        assert v is None
+    else:
+        assert v == round(rec["kernels"]["s2o_attn_fwd (S2O schedule)"]["mfma_busy"], 4)
+        assert 0.0 < v < 1.0

@@ -163,7 +163,10 @@ def gather_figure(attn_ms):
             "counts": "FETCH_SIZE + WRITE_SIZE beyond L2, Infinity Cache hits included"}
 
 
-def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles, rows_of=None):
+IMPORTANT_MASS = 0.9  # a row's important keys: the fewest history keys holding this share of its mass
+
+
+def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles, rows_of=None, exec_by_tau=None):
     """How well a tile's list order matches each row's true attention order.
 
     For every sampled tile (b, h, t) with history a > 0, E is the set of history
@@ -175,12 +178,21 @@ def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles, rows_of=None):
       coverage  sum_{j in E} e^x_ij / sum_{j < a} e^x_ij        (history mass executed)
       spearman  rank correlation between list position and -x_ij
     averaged over rows and tiles.  Plain numpy in fp32 from the bf16 inputs.
+    exec_by_tau (optional): {tau: executed tile counts of `tiles`, in order};
+    for each tau, with E_tau the keys executed at that tau and I_i the fewest
+    history keys holding IMPORTANT_MASS of row i's history mass,
+      precision |E_tau intersect I_i| / |E_tau|,  recall |E_tau intersect I_i| / |I_i|,
+      coverage as above,
+    averaged over rows and tiles (precision over tiles with E_tau non-empty),
+    returned under "by_tau" in decreasing tau.
     """
     from long_context_prefill_amd import synth
     BN = w.tile_n
     G = w.Hq // w.Hkv
     acc = {"overlap": [], "mass": [], "coverage": [], "spearman": []}
-    for (b, h, t) in tiles:
+    taus = sorted(exec_by_tau, reverse=True) if exec_by_tau else []
+    per_tau = {tau: {"precision": [], "recall": [], "coverage": []} for tau in taus}
+    for ti_, (b, h, t) in enumerate(tiles):
         a = (t * w.tile_m // w.seg_len) * w.seg_len
         if a == 0:
             continue
@@ -206,10 +218,30 @@ def ranking_study(w, x, lists, idx, offsets, exec_tiles, tiles, rows_of=None):
         acc["coverage"].append(float(np.mean(ex[:, E].sum(axis=1) / ex.sum(axis=1))))
         pos = np.empty(a, dtype=np.float64)
         pos[order] = np.arange(a)
-        rk = np.argsort(np.argsort(-xl, axis=1), axis=1).astype(np.float64)
+        srt = np.argsort(-xl, axis=1)                                       # keys by true order, per row
+        rk = np.empty(srt.shape, dtype=np.float64)                          # each key's true rank
+        rk[np.arange(srt.shape[0])[:, None], srt] = np.arange(a, dtype=np.float64)[None, :]
         pc, rc = pos - pos.mean(), rk - rk.mean(axis=1, keepdims=True)
         acc["spearman"].append(float(np.mean((rc @ pc) / (np.sqrt((rc ** 2).sum(axis=1)) * np.sqrt((pc ** 2).sum())))))
-    return {k: round(float(np.mean(v)), 4) for k, v in acc.items()} | {"tiles": len(acc["mass"])}
+        if taus:
+            cum = np.cumsum(np.take_along_axis(ex, srt, 1), axis=1)
+            m_i = (cum < IMPORTANT_MASS * cum[:, -1:]).sum(axis=1) + 1      # |I_i|
+            in_i = np.arange(a)[None, :] < m_i[:, None]                      # I_i in sorted coordinates
+            for tau in taus:
+                n_t = int(exec_by_tau[tau][ti_]) - p1
+                e_t = np.zeros(a, dtype=bool)
+                e_t[order[:n_t * BN]] = True
+                hit = (e_t[srt] & in_i).sum(axis=1)
+                if n_t > 0:
+                    per_tau[tau]["precision"].append(float(np.mean(hit / (n_t * BN))))
+                per_tau[tau]["recall"].append(float(np.mean(hit / m_i)))
+                per_tau[tau]["coverage"].append(float(np.mean(ex[:, e_t].sum(axis=1) / ex.sum(axis=1))))
+    out = {k: round(float(np.mean(v)), 4) for k, v in acc.items()} | {"tiles": len(acc["mass"])}
+    if taus:
+        out["important_mass"] = IMPORTANT_MASS
+        out["by_tau"] = [{"tau": tau} | {k: (round(float(np.mean(v)), 4) if v else None)
+                                         for k, v in per_tau[tau].items()} for tau in taus]
+    return out
 
 
 def cpu_baseline(w, x, tau, exec_gpu, n_tiles):
@@ -294,8 +326,13 @@ def main():
         exec_tiles = torch.empty((w.B, w.Hq, T), dtype=torch.int32, device="cuda")
         s2o.s2o_score(p, q, k, scores, ws_score)
         s2o.s2o_build_index(p, scores, idx, ws_sort)
+        study_exec = {}  # tau -> executed tiles of the ranking study's tiles
+
         def evaluate(tau):
             s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles)
+            if not args.no_ranking_study:
+                et = exec_tiles.cpu().numpy()
+                study_exec[tau] = [int(et[b_, h_, t_]) for (b_, h_, t_) in study_tiles]
             mse = float(((out.float() - out_dense.float()) ** 2).mean())
             density = float(exec_tiles.sum()) / dense_tiles
             log(f"[{mode}] tau {tau:g}: density {density:.4f} mse {mse:.3e}")
@@ -346,7 +383,8 @@ def main():
                 o_ = n_keys + (b_ * w.Hq + h_) * w.N + t_ * w.tile_m
                 return a_ + idx_h[o_:o_ + w.tile_m].astype(np.int64)
             study = ranking_study(w, x, lists, idx_h, lambda b_, h_, t_: s2o.list_offset(p, b_, h_, t_),
-                                  exec_tiles.cpu().numpy(), study_tiles, rows_of if qperm else None)
+                                  exec_tiles.cpu().numpy(), study_tiles, rows_of if qperm else None,
+                                  exec_by_tau=study_exec)
         log(f"[{mode}] step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index "
             f"{sort_ms:.2f} + attn {attn_ms:.2f}")
         res = {"tau": tau, "ms_per_step": ms_per_step, "score_ms": score_ms, "sort_ms": sort_ms,

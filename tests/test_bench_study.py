@@ -116,3 +116,40 @@ def test_mfma_busy_counter_reads_the_matching_profile():
     else:
         assert v == round(rec["kernels"]["s2o_attn_fwd (S2O schedule)"]["mfma_busy"], 4)
         assert 0.0 < v < 1.0
+
+
+def _run_by_tau(order_fn, chunks_by_tau):
+    w, x, qrow = _problem()
+    T = w.N // w.tile_m
+    t = T - 1
+    a = (t * w.tile_m // w.seg_len) * w.seg_len
+    true_order = np.argsort(-(x["k"][0, 0, :a] @ qrow), kind="stable").astype(np.int32)
+    idx = np.zeros(1 << 12, np.int32)
+    idx[:a] = order_fn(true_order)
+    p1 = ((t + 1) * w.tile_m - a) // w.tile_n
+    exec_tiles = np.zeros((1, 1, T), np.int32)
+    exec_tiles[0, 0, t] = p1 + max(chunks_by_tau.values())
+    by_tau = {tau: [p1 + n] for tau, n in chunks_by_tau.items()}
+    return bench.ranking_study(w, x, "tile", idx, lambda b, h, tt: 0, exec_tiles, [(0, 0, t)],
+                               exec_by_tau=by_tau), a, w.tile_n
+
+
+def test_by_tau_precision_and_recall_follow_the_definitions():
+    # true order: the first chunk lies inside every row's important set (precision 1),
+    # executing every chunk recalls all of it and covers the whole history
+    r, a, bn = _run_by_tau(lambda o: o, {1e-2: 1, 0.0: 256 // 64})  # history 256 keys = 4 chunks
+    rows = {e["tau"]: e for e in r["by_tau"]}
+    assert [e["tau"] for e in r["by_tau"]] == [1e-2, 0.0]
+    assert rows[1e-2]["precision"] == 1.0 and 0.0 < rows[1e-2]["recall"] < 1.0
+    assert rows[0.0]["recall"] == 1.0 and rows[0.0]["coverage"] == 1.0
+    assert rows[0.0]["precision"] < 1.0
+    assert rows[1e-2]["coverage"] < rows[0.0]["coverage"]
+    # reversed order: the first chunk holds the least important keys
+    rr, _, _ = _run_by_tau(lambda o: o[::-1].copy(), {1e-2: 1})
+    assert rr["by_tau"][0]["precision"] < rows[1e-2]["precision"]
+    assert rr["by_tau"][0]["recall"] < rows[1e-2]["recall"]
+
+
+def test_study_without_taus_has_no_table():
+    r = _run(lambda o, a, bn: o, n_chunks=2)
+    assert "by_tau" not in r

@@ -18,6 +18,8 @@ Parity status of each function (the pins live in ``tests/test_oracle_pins.py``):
   torch's fp64 SDPA; Q = 0 closed form of the stop rule including the equality
   case; restricted-softmax identity; skipped-mass bounds).
 * ``dense_rows``: pinned (torch fp64 SDPA and a numpy softmax).
+* shared (GQA) lists: pinned (exact dyadic group means; every head of a group
+  reads one list; G = 1 equals per-head lists; tau = 0 equals dense attention).
 """
 
 from __future__ import annotations
@@ -51,7 +53,7 @@ class Problem(ctypes.Structure):
                 ("seg_len", ctypes.c_int32), ("tile_m", ctypes.c_int32),
                 ("tile_n", ctypes.c_int32), ("scale", ctypes.c_double),
                 ("per_segment", ctypes.c_int32), ("block_lists", ctypes.c_int32),
-                ("qperm", ctypes.c_int32)]
+                ("qperm", ctypes.c_int32), ("share_gqa", ctypes.c_int32)]
 
 
 _lib = None
@@ -100,20 +102,24 @@ def _load():
 
 
 def problem(B, Hq, Hkv, N, d, dtype, seg_len, tile_m, tile_n, scale, per_segment=False,
-            block_lists=False, qperm=False) -> Problem:
+            block_lists=False, qperm=False, share_gqa=False) -> Problem:
     """dtype: "f32" (float32 arrays) or "bf16" (uint16 bit-pattern arrays).
     per_segment: one list per segment (shared by its tiles) instead of per tile.
     block_lists: list entries are blocks of tile_n keys instead of keys.
-    qperm: query rows ordered within each segment by a guide score (Q_perm)."""
+    qperm: query rows ordered within each segment by a guide score (Q_perm).
+    share_gqa: one list per KV head, shared by its query heads (not with qperm)."""
+    if qperm and share_gqa:
+        raise ValueError("shared lists are not defined with the query permutation")
     return Problem(B, Hq, Hkv, N, d, 0 if dtype == "f32" else 1, seg_len, tile_m, tile_n,
-                   float(scale), 1 if per_segment else 0, 1 if block_lists else 0, 1 if qperm else 0)
+                   float(scale), 1 if per_segment else 0, 1 if block_lists else 0, 1 if qperm else 0,
+                   1 if share_gqa else 0)
 
 
 def problem_from_workload(w, seg_len=None, per_segment=False, block_lists=False,
-                          qperm=False) -> Problem:
+                          qperm=False, share_gqa=False) -> Problem:
     return problem(w.B, w.Hq, w.Hkv, w.N, w.d, w.dtype,
                    w.seg_len if seg_len is None else seg_len, w.tile_m, w.tile_n, w.scale,
-                   per_segment, block_lists, qperm)
+                   per_segment, block_lists, qperm, share_gqa)
 
 
 def _ptr(a):

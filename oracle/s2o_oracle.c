@@ -36,6 +36,12 @@
  *              representative query of the segment): the mean of the
  *              segment's tile queries, an fp32 sum over its tiles in
  *              ascending order times fl(1/number of tiles).
+ *   shared lists (optional, with either granularity): one list per KV head
+ *              instead of per query head, used by the G query heads of the
+ *              group (a GQA form of KV_perm's shared index map); its
+ *              representative is the mean of the G heads' representatives, an
+ *              fp32 sum over the heads in ascending order from 0, times
+ *              fl(1/G).
  *   block lists (optional granularity): entries are blocks of BN consecutive
  *              history keys instead of single keys.  Block c is scored with
  *              its mean key (fp32 sum of its BN rows in ascending order, then
@@ -98,6 +104,8 @@ typedef struct {
     int32_t per_segment; /* 0: one list per query tile; 1: one list per segment */
     int32_t block_lists; /* 0: entries are keys; 1: entries are blocks of tile_n keys */
     int32_t qperm;       /* 1: query rows permuted within each segment (Q_perm) */
+    int32_t share_gqa;   /* 1: one list per (b, KV head, tile or segment), shared by the
+                            G query heads of the group (not with qperm) */
 } oracle_problem;
 
 /* ---- element access ------------------------------------------------------ */
@@ -156,8 +164,12 @@ static int64_t per_head_entries(const oracle_problem *p) {
     return total;
 }
 
+/* heads that own lists, and the list head of query head h */
+static int32_t list_heads(const oracle_problem *p) { return p->share_gqa ? p->Hkv : p->Hq; }
+static int32_t list_head(const oracle_problem *p, int h) { return p->share_gqa ? h / (p->Hq / p->Hkv) : h; }
+
 int64_t oracle_list_offset(const oracle_problem *p, int b, int h, int t) {
-    int64_t off = ((int64_t)b * p->Hq + h) * per_head_entries(p);
+    int64_t off = ((int64_t)b * list_heads(p) + list_head(p, h)) * per_head_entries(p);
     if (p->per_segment) {
         int seg = (int)(oracle_seg_start(p, t) / p->seg_len);
         for (int s = 0; s < seg; ++s) off += (int64_t)s * p->seg_len / entry_keys(p);
@@ -168,7 +180,7 @@ int64_t oracle_list_offset(const oracle_problem *p, int b, int h, int t) {
 }
 
 int64_t oracle_list_entries(const oracle_problem *p) {
-    int64_t n = (int64_t)p->B * p->Hq * per_head_entries(p);
+    int64_t n = (int64_t)p->B * list_heads(p) * per_head_entries(p);
     if (p->qperm) n += (int64_t)p->B * p->Hq * p->N; /* the query orders, after every key list */
     return n;
 }
@@ -177,7 +189,7 @@ int64_t oracle_list_entries(const oracle_problem *p) {
  * lists, one run of N entries per (b, h), segment by segment; entries are
  * row numbers relative to the segment start. */
 int64_t oracle_query_list_offset(const oracle_problem *p, int b, int h, int s) {
-    return (int64_t)p->B * p->Hq * per_head_entries(p) + ((int64_t)b * p->Hq + h) * p->N +
+    return (int64_t)p->B * list_heads(p) * per_head_entries(p) + ((int64_t)b * p->Hq + h) * p->N +
            (int64_t)s * p->seg_len;
 }
 
@@ -256,7 +268,8 @@ void oracle_pool(const oracle_problem *p, const void *Q, const void *K, int b, i
 /* Representative query of the list tile t uses: the tile's mean, or (segment
  * lists) the mean of the segment's tile means: fp32 sum over the segment's
  * tiles in ascending order, then one multiplication by fl(1/number of tiles). */
-void oracle_rep_query(const oracle_problem *p, const void *Q, const void *K, int b, int h, int t, float *qbar) {
+static void rep_query_head(const oracle_problem *p, const void *Q, const void *K, int b, int h, int t,
+                           float *qbar) {
     if (!p->per_segment) {
         oracle_pool(p, Q, K, b, h, t, qbar);
         return;
@@ -274,6 +287,26 @@ void oracle_rep_query(const oracle_problem *p, const void *Q, const void *K, int
     float inv = 1.0f / (float)(last - first);
     for (int k = 0; k < p->d; ++k) qbar[k] = qbar[k] * inv;
     free(tq);
+}
+
+/* Shared lists: the mean of the group's G per-head representatives (fp32 sum
+ * over the heads in ascending order from 0, then one multiplication by
+ * fl(1/G)); otherwise the head's own representative. */
+void oracle_rep_query(const oracle_problem *p, const void *Q, const void *K, int b, int h, int t, float *qbar) {
+    if (!p->share_gqa) {
+        rep_query_head(p, Q, K, b, h, t, qbar);
+        return;
+    }
+    int G = p->Hq / p->Hkv, h0 = (h / G) * G;
+    float *hq = (float *)malloc(sizeof(float) * p->d);
+    for (int k = 0; k < p->d; ++k) qbar[k] = 0.0f;
+    for (int j = 0; j < G; ++j) {
+        rep_query_head(p, Q, K, b, h0 + j, t, hq);
+        for (int k = 0; k < p->d; ++k) qbar[k] = qbar[k] + hq[k];
+    }
+    float inv = 1.0f / (float)G;
+    for (int k = 0; k < p->d; ++k) qbar[k] = qbar[k] * inv;
+    free(hq);
 }
 
 /* Mean key of block c (keys c*BN .. c*BN+BN-1) of KV head g: fp32 sum of the
@@ -494,11 +527,11 @@ static int lists_per_head(const oracle_problem *p) {
 
 /* scores of every list, in the list layout */
 void oracle_scores_all(const oracle_problem *p, const void *Q, const void *K, float *scores) {
-    int32_t U = lists_per_head(p);
-    int64_t units = (int64_t)p->B * p->Hq * U;
+    int32_t U = lists_per_head(p), LH = list_heads(p), G = p->Hq / LH;
+    int64_t units = (int64_t)p->B * LH * U;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t u = 0; u < units; ++u) {
-        int b = (int)(u / ((int64_t)p->Hq * U)), h = (int)((u / U) % p->Hq);
+        int b = (int)(u / ((int64_t)LH * U)), h = (int)((u / U) % LH) * G; /* first head using the list */
         int t = list_owner(p, (int)(u % U));
         if (oracle_list_len(p, t) > 0)
             oracle_score_tile(p, Q, K, b, h, t, scores + oracle_list_offset(p, b, h, t));
@@ -514,11 +547,11 @@ void oracle_scores_all(const oracle_problem *p, const void *Q, const void *K, fl
 
 /* every list from the scores */
 void oracle_lists_all(const oracle_problem *p, const float *scores, int32_t *lists) {
-    int32_t U = lists_per_head(p);
-    int64_t units = (int64_t)p->B * p->Hq * U;
+    int32_t U = lists_per_head(p), LH = list_heads(p), G = p->Hq / LH;
+    int64_t units = (int64_t)p->B * LH * U;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t u = 0; u < units; ++u) {
-        int b = (int)(u / ((int64_t)p->Hq * U)), h = (int)((u / U) % p->Hq);
+        int b = (int)(u / ((int64_t)LH * U)), h = (int)((u / U) % LH) * G; /* first head using the list */
         int t = list_owner(p, (int)(u % U));
         int64_t off = oracle_list_offset(p, b, h, t);
         oracle_order(scores + off, oracle_list_len(p, t), lists + off);

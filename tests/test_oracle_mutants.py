@@ -56,6 +56,11 @@ MUTANTS = {
     "pass 1 stops at the tile's first row": ("        if (rows[r] > last) last = rows[r];", "        if (rows[r] < last) last = rows[r];"),
     "query score with the wrong head": ("acc = fmaf(widen(Q, p->dtype, q_index(p, b, h, a + i, k)), guide[k], acc);",
                                         "acc = fmaf(widen(Q, p->dtype, q_index(p, b, (h + 1) % p->Hq, a + i, k)), guide[k], acc);"),
+    "shared representative drops a head": ("for (int j = 0; j < G; ++j) {\n        rep_query_head",
+                                           "for (int j = 1; j < G; ++j) {\n        rep_query_head"),
+    "shared lists laid out per query head": (
+        "static int32_t list_head(const oracle_problem *p, int h) { return p->share_gqa ? h / (p->Hq / p->Hkv) : h; }",
+        "static int32_t list_head(const oracle_problem *p, int h) { return p->share_gqa ? h % p->Hkv : h; }"),
     "block scored by its first key": ("            oracle_pool_block(p, K, b, g, j, kbar);",
                                       "            for (int k = 0; k < p->d; ++k) kbar[k] = widen(K, p->dtype, kv_index(p, b, g, j * p->tile_n, k));"),
 }

@@ -520,6 +520,82 @@ def test_segment_representative_exact_on_dyadic_inputs():
         assert [Fraction(float(x)) for x in oracle.rep_query(p, Q, 0, 0, t)] == want
 
 
+# ------------------------------------------------------- shared (GQA) lists ---
+# One list per KV head (per tile or per segment), read by the G query heads of
+# the group and ranked against the mean of their representatives: KV_perm's
+# index map shared at the granularity at which the heads share K and V
+# (gist.science summary, "Classement par Segment").
+
+@pytest.mark.parametrize("geom", GEOMS)
+def test_shared_lists_tau_zero_equals_dense_attention(geom):
+    B, Hq, Hkv, N, d, S, BM, BN, dt = geom
+    Q, K, V = random_inputs(B, Hq, Hkv, N, d, seed=141 + N, dtype=dt)
+    for per_segment in (False, True):
+        p = oracle.problem(B, Hq, Hkv, N, d, dt, S, BM, BN, 1 / np.sqrt(d), per_segment=per_segment,
+                           share_gqa=True)
+        out, _, _, _ = run_all(p, Q, K, V, 0.0)
+        np.testing.assert_allclose(out, sdpa_fp64(p, Q, K, V), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("per_segment", [False, True])
+def test_shared_list_layout_and_sharing(per_segment):
+    """Offsets walk (b, KV head, list); every query head of a group reads the same list,
+    the order of the group representative's scores."""
+    B, Hq, Hkv, N, d, S, BM = 2, 4, 2, 200, 16, 48, 8
+    Q, K, V = random_inputs(B, Hq, Hkv, N, d, seed=19)
+    p = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, 8, 0.25, per_segment=per_segment, share_gqa=True)
+    ph = oracle.problem(B, Hq, Hkv, N, d, "f32", S, BM, 8, 0.25, per_segment=per_segment)
+    L = oracle.list_entries(ph) // (B * Hq)
+    assert oracle.list_entries(p) == B * Hkv * L
+    scores = oracle.scores_all(p, Q, K)
+    lists = oracle.lists_all(p, scores)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(N // BM):
+                off = oracle.list_offset(p, b, h, t)
+                assert off == (b * Hkv + h // G) * L + oracle.list_offset(ph, 0, 0, t)
+                a = oracle.seg_start(p, t)
+                sc = oracle.score_tile(p, Q, K, b, h, t)
+                assert np.array_equal(scores[off:off + a], sc)
+                assert np.array_equal(lists[off:off + a], oracle.order(sc))
+                assert np.array_equal(oracle.rep_query(p, Q, b, h, t), oracle.rep_query(p, Q, b, h // G * G, t))
+
+
+def test_shared_representative_exact_on_dyadic_inputs():
+    """Constant integer rows per (head, tile), four heads per group and power-of-two
+    counts: every fp32 operation is exact, so the representative is the exact mean of
+    the group's tile values (per tile) or of its segment means (per segment)."""
+    Hq, Hkv, N, d, BM, S = 8, 2, 128, 4, 8, 32
+    rng = np.random.default_rng(4)
+    vals = rng.integers(-6, 7, size=(Hq, N // BM, d)).astype(np.float32)
+    Q = np.repeat(vals, BM, axis=1).reshape(1, Hq, N, d).astype(np.float32)
+    G = Hq // Hkv
+    for per_segment in (False, True):
+        p = oracle.problem(1, Hq, Hkv, N, d, "f32", S, BM, 8, 1.0, per_segment=per_segment, share_gqa=True)
+        for h in (0, 5):
+            for t in range(N // BM):
+                heads = range(h // G * G, h // G * G + G)
+                if per_segment:
+                    first = t * BM // S * (S // BM)
+                    tiles = range(first, first + S // BM)
+                else:
+                    tiles = [t]
+                want = [sum(Fraction(int(vals[hh, tt, k])) for hh in heads for tt in tiles) /
+                        (G * len(tiles)) for k in range(d)]
+                assert [Fraction(float(x)) for x in oracle.rep_query(p, Q, 0, h, t)] == want
+
+
+def test_shared_lists_with_one_head_per_group_equal_per_head_lists():
+    """G = 1: the shared form is the per-head form, bit for bit."""
+    Q, K, V = random_inputs(1, 2, 2, 256, 16, seed=23, dtype="bf16")
+    for per_segment in (False, True):
+        a = oracle.problem(1, 2, 2, 256, 16, "bf16", 64, 16, 16, 0.25, per_segment=per_segment)
+        s = oracle.problem(1, 2, 2, 256, 16, "bf16", 64, 16, 16, 0.25, per_segment=per_segment, share_gqa=True)
+        assert oracle.list_entries(a) == oracle.list_entries(s)
+        assert np.array_equal(oracle.scores_all(a, Q, K).view(np.uint32), oracle.scores_all(s, Q, K).view(np.uint32))
+
+
 # ------------------------------------------------------------- block lists ---
 # List entries are blocks of BN consecutive keys, scored with the block's mean
 # key; pass-2 chunk c is the c-th listed block.  The pages contrast S2O's

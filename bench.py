@@ -108,7 +108,7 @@ def parse():
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--tile-lists-only", action="store_true",
                     help="skip the per-segment-list measurement")
-    ap.add_argument("--modes", default="segment,tile_blocks,tile+qperm",
+    ap.add_argument("--modes", default="segment,tile_blocks,tile+qperm,tile+gqa",
                     help="list forms measured besides the headline per-tile lists")
     ap.add_argument("--no-ranking-study", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -313,10 +313,11 @@ def main():
 
     def run_mode(mode, steps, warmup, tau_fixed):
         """tau sweep (untimed), then `steps` timed steps of score -> build_index -> attention.
-        mode: a list form ("tile", "segment", "tile_blocks", ...), "+qperm" for Q_perm."""
-        lists, qperm = mode.split("+")[0], mode.endswith("+qperm")
+        mode: a list form ("tile", "segment", "tile_blocks", ...), "+qperm" for Q_perm,
+        "+gqa" for lists shared by the query heads of a KV head."""
+        lists, qperm, share = mode.split("+")[0], mode.endswith("+qperm"), mode.endswith("+gqa")
         p = s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0, w.seg_len,
-                        w.tile_m, w.tile_n, w.scale, lists=lists, qperm=qperm)
+                        w.tile_m, w.tile_n, w.scale, lists=lists, qperm=qperm, share_gqa=share)
         n_list = s2o.list_entries(p)
         scores = torch.empty(max(n_list, 1), dtype=torch.float32, device="cuda")
         idx = torch.empty(max(n_list, 1), dtype=torch.int32, device="cuda")
@@ -444,7 +445,8 @@ def main():
     }
     names = {"segment": "segment_lists", "tile_blocks": "block_lists",
              "segment_blocks": "segment_block_lists", "tile+qperm": "query_permutation",
-             "segment+qperm": "segment_lists_query_permutation"}
+             "segment+qperm": "segment_lists_query_permutation", "tile+gqa": "shared_lists",
+             "segment+gqa": "segment_shared_lists"}
     for m, r in extra.items():
         rec[names.get(m, m + "_lists")] = {
             "ms_per_step": round(r["ms_per_step"], 3), "tau": r["tau"],

@@ -78,7 +78,8 @@ typedef struct {
     int32_t tile_m;   /* BM: 64 or 128 */
     int32_t tile_n;   /* BN: 64 */
     float scale;      /* softmax scale (1/sqrt(d) for standard attention), finite */
-    int32_t list_granularity; /* one of the S2O_LISTS_* values below */
+    int32_t list_granularity; /* one of the S2O_LISTS_* values below, optionally ORed with
+                                 S2O_QUERY_PERMUTATION or S2O_SHARE_GQA */
 } s2o_problem;
 
 /* Which query a list is ranked against ([GIST] KV_perm), and what an entry is.
@@ -115,13 +116,23 @@ enum {
  * bf16 problems with seg_len <= 8192 only (else S2O_ERR_UNSUPPORTED). */
 enum { S2O_QUERY_PERMUTATION = 4 };
 
+/* Flag to OR into list_granularity: shared lists (the GQA form of [GIST]
+ * KV_perm's shared index map).  One list per (b, KV head, tile or segment)
+ * instead of per query head, read by the G query heads of the group; it is
+ * ranked against the mean of the G heads' representatives (fp32 sum over the
+ * heads in ascending order from 0, times fl(1/G)).  Lists are laid out as
+ * above with (b*Hkv + h/G) in place of (b*Hq + h), so there are B*Hkv*L
+ * entries.  Not with S2O_QUERY_PERMUTATION (S2O_ERR_UNSUPPORTED). */
+enum { S2O_SHARE_GQA = 8 };
+
 /* Validates a problem (sizes, divisibility, supported tiles).  Returns S2O_OK,
  * S2O_ERR_INVALID_ARG or S2O_ERR_UNSUPPORTED.  Pure host function. */
 s2o_status s2o_check_problem(const s2o_problem *p);
 
 /* Total list entries over all lists (per tile: B*Hq*sum_t a_t; per segment:
- * B*Hq*sum_s s*S; divided by tile_n for block lists; plus B*Hq*N query-order
- * entries with S2O_QUERY_PERMUTATION).  -1 if the problem is invalid.  Pure
+ * B*Hq*sum_s s*S; Hkv in place of Hq with S2O_SHARE_GQA; divided by tile_n
+ * for block lists; plus B*Hq*N query-order entries with
+ * S2O_QUERY_PERMUTATION).  -1 if the problem is invalid.  Pure
  * host function. */
 int64_t s2o_list_entries(const s2o_problem *p);
 

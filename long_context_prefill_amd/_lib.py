@@ -86,29 +86,31 @@ def _raise(fn: str, st: int):
 
 LISTS = {"tile": 0, "segment": 1, "tile_blocks": 2, "segment_blocks": 3}
 QUERY_PERMUTATION = 4
+SHARE_GQA = 8
 LISTS_PER_TILE, LISTS_PER_SEGMENT = LISTS["tile"], LISTS["segment"]
 
 
 def problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, seg_len, tile_m=128,
-            tile_n=64, scale=None, causal=True, lists="tile", qperm=False) -> Problem:
+            tile_n=64, scale=None, causal=True, lists="tile", qperm=False, share_gqa=False) -> Problem:
     """dtype: torch.float32 / torch.bfloat16 (or 0 / 1).
     lists: "tile" (one list per query tile), "segment" (one list per segment), or
     "tile_blocks" / "segment_blocks" (the same with blocks of tile_n keys as entries).
-    qperm: order the query rows of every segment by their guide score (Q_perm)."""
+    qperm: order the query rows of every segment by their guide score (Q_perm).
+    share_gqa: one list per KV head, read by its query heads (S2O_SHARE_GQA)."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
-    gran = LISTS[lists] | (QUERY_PERMUTATION if qperm else 0)
+    gran = LISTS[lists] | (QUERY_PERMUTATION if qperm else 0) | (SHARE_GQA if share_gqa else 0)
     return Problem(batch, heads_q, heads_kv, seq_len, head_dim, dtype, 1 if causal else 0,
                    seg_len, tile_m, tile_n, float(scale), gran)
 
 
 def problem_for(q: torch.Tensor, k: torch.Tensor, seg_len: int, tile=(128, 64), scale=None,
-                causal=True, lists="tile", qperm=False) -> Problem:
+                causal=True, lists="tile", qperm=False, share_gqa=False) -> Problem:
     B, Hq, N, d = q.shape
     return problem(B, Hq, k.shape[1], N, d, q.dtype, seg_len, tile[0], tile[1], scale, causal,
-                   lists, qperm)
+                   lists, qperm, share_gqa)
 
 
 def _stream() -> ctypes.c_void_p:
@@ -219,9 +221,9 @@ def dense_attn_fwd(p: Problem, q, k, v, out=None) -> torch.Tensor:
 
 
 def s2o_attention(q, k, v, tau: float, seg_len: int, tile=(128, 64), scale=None, lists="tile",
-                  qperm=False):
+                  qperm=False, share_gqa=False):
     """Whole path: score -> build_index -> attention.  Returns (O, exec_tiles)."""
-    p = problem_for(q, k, seg_len, tile, scale, lists=lists, qperm=qperm)
+    p = problem_for(q, k, seg_len, tile, scale, lists=lists, qperm=qperm, share_gqa=share_gqa)
     scores = s2o_score(p, q, k)
     idx = s2o_build_index(p, scores)
     return s2o_attn_fwd(p, q, k, v, idx, tau)

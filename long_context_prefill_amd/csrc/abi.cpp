@@ -13,6 +13,13 @@ bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The problem scoring and sorting see: shared lists as one query head per KV
+// head, block lists as a problem whose keys are blocks.
+Geometry list_geometry(const Geometry &g) {
+    const Geometry r = s2o::group_geometry(g);
+    return g.blocks ? s2o::block_geometry(r) : r;
+}
+
 // Fills g from p, or returns the reason it cannot.
 s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     if (!p) return S2O_ERR_INVALID_ARG;
@@ -30,9 +37,11 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     if (p->head_dim != 64 && p->head_dim != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_m != 64 && p->tile_m != 128) return S2O_ERR_UNSUPPORTED;
     if (p->tile_n != s2o::kTileN) return S2O_ERR_UNSUPPORTED;
-    if (p->list_granularity < 0 || p->list_granularity > 7) return S2O_ERR_INVALID_ARG;
+    if (p->list_granularity < 0 || p->list_granularity > 15) return S2O_ERR_INVALID_ARG;
     if ((p->list_granularity & S2O_QUERY_PERMUTATION) &&
         (p->dtype != S2O_BF16 || p->seg_len > s2o::kQuerySortCap))
+        return S2O_ERR_UNSUPPORTED;
+    if ((p->list_granularity & S2O_QUERY_PERMUTATION) && (p->list_granularity & S2O_SHARE_GQA))
         return S2O_ERR_UNSUPPORTED;
 
     g.B = p->batch;
@@ -52,6 +61,7 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     g.per_seg = p->list_granularity & 1;
     g.blocks = (p->list_granularity >> 1) & 1;
     g.qperm = (p->list_granularity >> 2) & 1;
+    g.share = (p->list_granularity >> 3) & 1;
     g.nseg = (g.N + g.S - 1) / g.S;
     g.inv_P = 1.0f / (float)g.P;
     g.inv_P_last = 1.0f / (float)(g.T - (g.nseg - 1) * g.P);
@@ -65,7 +75,7 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
     }
     if (g.blocks) L /= g.BN;  // every history is a multiple of S, and S of BN
     g.list_per_head = L;
-    g.list_entries = L * g.B * g.Hq;
+    g.list_entries = L * g.B * (g.share ? g.Hkv : g.Hq);
     g.query_entries = g.qperm ? (int64_t)g.B * g.Hq * g.N : 0;
     // index ranges the kernels assume (the attention kernel addresses one KV
     // head's K or V, and a tile's list, with 32-bit byte offsets)
@@ -75,7 +85,7 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
         return S2O_ERR_UNSUPPORTED;
     const int64_t nseg = (g.N + g.S - 1) / g.S;
     if ((int64_t)g.B * g.Hkv * nseg > 65535) return S2O_ERR_UNSUPPORTED;
-    const Geometry lg = g.blocks ? s2o::block_geometry(g) : g;
+    const Geometry lg = list_geometry(g);
     int64_t e = lg.S & (-lg.S);
     if (e > 4096) e = 4096;
     if (lg.list_entries / e >= (1ll << 31)) return S2O_ERR_UNSUPPORTED;
@@ -114,13 +124,16 @@ int64_t s2o_list_offset(const s2o_problem *p, int32_t b, int32_t h, int32_t t) {
 }
 
 namespace {
-Geometry list_geometry(const Geometry &g) { return g.blocks ? s2o::block_geometry(g) : g; }
 size_t tile_query_bytes(const Geometry &g) { return ((size_t)g.B * g.Hq * g.T * g.d * sizeof(float) + 255) & ~(size_t)255; }
 size_t segment_query_bytes(const Geometry &g) {
     return g.per_seg ? (((size_t)g.B * g.Hq * g.nseg * g.d * sizeof(float) + 255) & ~(size_t)255) : 0;
 }
 size_t block_key_bytes(const Geometry &g) {
     return g.blocks ? (((size_t)g.B * g.Hkv * (g.N / g.BN) * g.d * sizeof(float) + 255) & ~(size_t)255) : 0;
+}
+size_t group_query_bytes(const Geometry &g) {
+    return g.share ? (((size_t)g.B * g.Hkv * (g.per_seg ? g.nseg : g.T) * g.d * sizeof(float) + 255) & ~(size_t)255)
+                   : 0;
 }
 size_t guide_bytes(const Geometry &g) {
     return g.qperm ? (((size_t)g.B * g.Hkv * g.nseg * g.d * sizeof(float) + 255) & ~(size_t)255) : 0;
@@ -134,7 +147,7 @@ size_t s2o_score_workspace_bytes(const s2o_problem *p) {
     Geometry g;
     if (make_geometry(p, g) != S2O_OK) return 0;
     return tile_query_bytes(g) + segment_query_bytes(g) + block_key_bytes(g) + guide_bytes(g) +
-           query_order_bytes(g);
+           query_order_bytes(g) + group_query_bytes(g);
 }
 
 s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *scores,
@@ -155,6 +168,7 @@ s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *
     float *kbar = reinterpret_cast<float *>(after);
     float *guides = reinterpret_cast<float *>(after + block_key_bytes(g));
     int32_t *qorder = reinterpret_cast<int32_t *>(after + block_key_bytes(g) + guide_bytes(g));
+    float *qgrp = reinterpret_cast<float *>(after + block_key_bytes(g) + guide_bytes(g) + query_order_bytes(g));
     hipError_t e;
     if (g.qperm) {  // Q_perm: query scores (after the key lists) and the query order
         e = s2o::launch_query_scores(g, Q, K, guides, scores + g.list_entries, s);
@@ -165,11 +179,18 @@ s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *
     if (g.list_entries == 0) return S2O_OK;
     e = s2o::launch_pool(g, Q, g.qperm ? qorder : nullptr, qbar, qseg, s);
     if (e != hipSuccess) return S2O_ERR_HIP;
-    if (!g.blocks) return launch_status(s2o::launch_score(g, g.per_seg ? qseg : qbar, K, scores, s));
+    const float *rep = g.per_seg ? qseg : qbar;
+    if (g.share) {  // shared lists: one representative per KV head
+        e = s2o::launch_group_mean(g, rep, g.per_seg ? g.nseg : g.T, qgrp, s);
+        if (e != hipSuccess) return S2O_ERR_HIP;
+        rep = qgrp;
+    }
+    const Geometry sg = s2o::group_geometry(g);
+    if (!g.blocks) return launch_status(s2o::launch_score(sg, rep, K, scores, s));
     // block lists: score the blocks' mean keys as the keys of the block geometry
     e = s2o::launch_pool_blocks(g, K, kbar, s);
     if (e != hipSuccess) return S2O_ERR_HIP;
-    return launch_status(s2o::launch_score(s2o::block_geometry(g), g.per_seg ? qseg : qbar, kbar, scores, s));
+    return launch_status(s2o::launch_score(s2o::block_geometry(sg), rep, kbar, scores, s));
 }
 
 size_t s2o_build_index_workspace_bytes(const s2o_problem *p) {

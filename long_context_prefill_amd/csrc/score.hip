@@ -78,6 +78,23 @@ __global__ __launch_bounds__(256) void segpool_kernel(const float *__restrict__ 
     qseg[gid] = sum * (s == g.nseg - 1 ? g.inv_P_last : g.inv_P);
 }
 
+// Shared lists: the mean of the G per-head representatives of a group, an
+// fp32 sum over the heads in ascending order from 0 times fl(1/G).  One thread
+// per (b, KV head, row, k); rep is [B, Hq, rows, d], grp is [B, Hkv, rows, d].
+__global__ __launch_bounds__(256) void group_mean_kernel(const float *__restrict__ rep,
+                                                         float *__restrict__ grp, Geometry g, int rows,
+                                                         float inv_g, int64_t total) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= total) return;
+    const int64_t per_head = (int64_t)rows * g.d;
+    const int64_t bk = gid / per_head, in_head = gid % per_head;  // bk = b*Hkv + kvh
+    const int64_t b = bk / g.Hkv, kvh = bk % g.Hkv;
+    const float *src = rep + ((b * g.Hq + kvh * g.G) * per_head) + in_head;
+    float sum = 0.0f;
+    for (int j = 0; j < g.G; ++j) sum = sum + src[j * per_head];
+    grp[gid] = sum * inv_g;
+}
+
 // Block lists: the mean key of every block of BN keys, fp32 sum of its rows in
 // ascending order times 1/BN (exact: BN is a power of two), stored
 // [B, Hkv, N/BN, d] in the natural layout so the score kernel reads it as keys.
@@ -448,6 +465,14 @@ hipError_t launch_query_scores(const Geometry &g, const void *Q, const void *K, 
 hipError_t launch_query_sort(const Geometry &g, const float *qscores, int32_t *qorder, hipStream_t stream) {
     hipLaunchKernelGGL(query_sort_kernel, dim3((unsigned)((int64_t)g.B * g.Hq * g.nseg)), dim3(QSORT_THREADS), 0,
                        stream, qscores, qorder, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_mean(const Geometry &g, const float *rep, int rows, float *grp, hipStream_t stream) {
+    const int64_t total = (int64_t)g.B * g.Hkv * rows * g.d;
+    const float inv_g = 1.0f / (float)g.G;  // fl(1/G), rounded on the host
+    hipLaunchKernelGGL(group_mean_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, rep, grp,
+                       g, rows, inv_g, total);
     return hipGetLastError();
 }
 

@@ -40,24 +40,26 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def gpu_problem(w, seg_len=None, lists="tile", qperm=False):
+def gpu_problem(w, seg_len=None, lists="tile", qperm=False, share_gqa=False):
     return s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0,
                        w.seg_len if seg_len is None else seg_len, w.tile_m, w.tile_n, w.scale,
-                       lists=lists, qperm=qperm)
+                       lists=lists, qperm=qperm, share_gqa=share_gqa)
 
 
 class GpuRun:
     """Inputs on the device plus scores and lists from the HIP path."""
 
-    def __init__(self, w, x, seg_len=None, lists="tile", qperm=False):
+    def __init__(self, w, x, seg_len=None, lists="tile", qperm=False, share_gqa=False):
         self.w = w
         self.lists = lists
-        self.p = gpu_problem(w, seg_len, lists, qperm)
+        self.p = gpu_problem(w, seg_len, lists, qperm, share_gqa)
         self.po = oracle.problem_from_workload(w, seg_len, per_segment=lists.startswith("segment"),
-                                               block_lists=lists.endswith("blocks"), qperm=qperm)
+                                               block_lists=lists.endswith("blocks"), qperm=qperm,
+                                               share_gqa=share_gqa)
         self.x = x
         self.q, self.k, self.v = (to_device(x[n]) for n in ("q", "k", "v"))
-        say(f"{w.name}: score + build_index ({lists} lists, {s2o.list_entries(self.p)} entries)")
+        say(f"{w.name}: score + build_index ({lists} lists{', shared' if share_gqa else ''}, "
+            f"{s2o.list_entries(self.p)} entries)")
         self.scores = s2o.s2o_score(self.p, self.q, self.k)
         self.idx = s2o.s2o_build_index(self.p, self.scores)
         torch.cuda.synchronize()

@@ -92,6 +92,26 @@ def test_block_list_layout_matches_oracle_walk(N, S, BM, B, Hq, lists):
                 assert s2o.list_offset(p, b, h, t) == oracle.list_offset(po, b, h, t)
 
 
+@pytest.mark.parametrize("lists", ["tile", "segment", "tile_blocks", "segment_blocks"])
+@pytest.mark.parametrize("N,S,BM,B,Hq,Hkv", [(1024, 256, 128, 1, 4, 2), (2048, 512, 64, 2, 6, 2),
+                                             (64 * 63, 384, 64, 1, 2, 1), (131072, 8192, 128, 1, 32, 8)])
+def test_shared_list_layout_matches_oracle_walk(N, S, BM, B, Hq, Hkv, lists):
+    """Shared lists: one run per (b, KV head), read by every query head of the group."""
+    p = base_problem(batch=B, heads_q=Hq, heads_kv=Hkv, seq_len=N, seg_len=S, tile_m=BM, lists=lists,
+                     share_gqa=True)
+    assert s2o.check_problem(p) == 0
+    po = oracle.problem(B, Hq, Hkv, N, 128, "bf16", S, BM, 64, 1.0, per_segment=lists.startswith("segment"),
+                        block_lists=lists.endswith("blocks"), share_gqa=True)
+    ph = base_problem(batch=B, heads_q=Hq, heads_kv=Hkv, seq_len=N, seg_len=S, tile_m=BM, lists=lists)
+    assert s2o.list_entries(p) == oracle.list_entries(po) == s2o.list_entries(ph) // (Hq // Hkv)
+    T, G = N // BM, Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for t in sorted({0, T // 3, T // 2, T - 1}):
+                off = s2o.list_offset(p, b, h, t)
+                assert off == oracle.list_offset(po, b, h, t) == s2o.list_offset(p, b, h // G * G, t)
+
+
 def test_workspace_sizes():
     p = base_problem()
     assert s2o.score_workspace_bytes(p) == 1 * 4 * (1024 // 128) * 128 * 4
@@ -110,7 +130,8 @@ def test_workspace_sizes():
     ("batch", 0, INVALID), ("heads_q", 3, INVALID), ("seq_len", 1000, INVALID),
     ("seg_len", 200, INVALID), ("head_dim", 96, UNSUPPORTED), ("tile_m", 256, UNSUPPORTED),
     ("tile_n", 32, UNSUPPORTED), ("dtype", 7, INVALID), ("causal", 2, INVALID),
-    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 8, INVALID), ("list_granularity", -1, INVALID),
+    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 16, INVALID), ("list_granularity", -1, INVALID),
+    ("list_granularity", 4 | 8, UNSUPPORTED),  # query permutation with shared lists
     ("seq_len", 1 << 23, UNSUPPORTED)])  # one head's K at d = 128 would span 2^31 bytes
 def test_problem_validation(field, value, code):
     p = base_problem()

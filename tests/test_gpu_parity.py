@@ -544,3 +544,52 @@ def test_llama8b_128k_query_permutation_sampled():
         o, ex = run.attn(tau)
         assert_report(compare(run, tiles, tau, o, ex, check_lists=(tau == 1.2e-3)), "bf16")
         del o, ex
+
+
+# ------------------------------------------------------- shared (GQA) lists --
+# One list per KV head, read by the G query heads of the group and ranked
+# against the mean of their representatives (S2O_SHARE_GQA).
+
+@pytest.mark.parametrize("lists", ["tile", "segment", "tile_blocks"])
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_bf16_shared_lists_every_tile(case, lists):
+    name, B, Hq, Hkv, N, d, BM, S, structure = case
+    w = synth.custom_workload(B=B, Hq=Hq, Hkv=Hkv, N=N, d=d, dtype="bf16", tile_m=BM, tile_n=64,
+                              seg_len=S, structure=structure, n_stripes=max(N // 100, 4),
+                              seed=900 + N + d, name=name)
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists=lists, share_gqa=True)
+    assert s2o.list_entries(run.p) == oracle.list_entries(run.po)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    for tau in (0.0, 1e-3, 3e-2):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, all_tiles(w), tau, o, ex), "bf16")
+
+
+def test_f32_shared_lists_every_tile():
+    """fp32 inputs (the staged attention kernel), two query heads per KV head."""
+    w = synth.custom_workload(B=1, Hq=4, Hkv=2, N=1024, d=64, dtype="f32", tile_m=64, tile_n=64,
+                              seg_len=256, structure="stripes", n_stripes=8, seed=911, name="f32_shared")
+    x = synth.make_inputs(w)
+    for lists in ("tile", "segment"):
+        run = GpuRun(w, x, lists=lists, share_gqa=True)
+        scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+        assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+        assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+        o, ex = run.attn(1e-3)
+        assert_report(compare(run, all_tiles(w), 1e-3, o, ex), "f32")
+
+
+def test_llama8b_16k_shared_lists():
+    w = synth.WORKLOADS["llama8b_n16k"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, share_gqa=True)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    tiles = sample_tiles(w, heads=(0, 9, 18, 27), n_random=16, seed=7)
+    for tau in (1e-2, 1e-3):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex), "bf16")

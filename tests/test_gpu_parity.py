@@ -593,3 +593,18 @@ def test_llama8b_16k_shared_lists():
     for tau in (1e-2, 1e-3):
         o, ex = run.attn(tau)
         assert_report(compare(run, tiles, tau, o, ex), "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_128k_shared_lists_sampled():
+    """Shared lists at the headline shape, in the configuration bench.py times."""
+    w = synth.WORKLOADS["llama8b_n128k"]
+    say("generating llama8b_n128k inputs")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, share_gqa=True)
+    tiles = sample_tiles(w, heads=(1, 26), n_random=8, seed=11)
+    for tau in (1.42e-3, 1e-2):
+        o, ex = run.attn(tau)
+        say(f"oracle on {len(tiles)} sampled tiles")
+        assert_report(compare(run, tiles, tau, o, ex, check_lists=(tau == 1.42e-3)), "bf16")
+        del o, ex

@@ -44,7 +44,8 @@ MSE_BUDGET = 1e-5
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_s2o_attn_fwd_llama8b_n128k.json")
-ATTN_SOURCE = os.path.join(ROOT, "long_context_prefill_amd", "csrc", "attn_fwd.hip")
+# the attention kernel's sources: its file and the shared geometry header it compiles
+ATTN_SOURCE = [os.path.join(ROOT, "long_context_prefill_amd", "csrc", f) for f in ("attn_fwd.hip", "s2o_internal.h")]
 
 
 def refine_tau(sweep, evaluate, budget=MSE_BUDGET, steps=4):
@@ -116,8 +117,12 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_hash(paths):
+    """First 16 hex digits of the SHA-256 of the files' contents, concatenated in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_figure():

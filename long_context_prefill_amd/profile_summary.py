@@ -45,6 +45,14 @@ def short(name: str) -> str:
     return f"{label} ({KERNELS[key]})" if KERNELS[key] else key
 
 
+def sources_hash(paths):
+    """First 16 hex digits of the SHA-256 of the files' contents, concatenated in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
 def per_kernel(path, value="Counter_Value"):
     agg = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
@@ -102,7 +110,7 @@ def main_counters(a):
         print(f"  per MFMA: {r['valu_insts_per_mfma']:.2f} other VALU ({r['trans_per_mfma']:.2f} "
               f"transcendental), {r['lds_insts_per_mfma']:.2f} LDS instructions\n")
     if a.json_out:
-        src = hashlib.sha256(open(a.source, "rb").read()).hexdigest()[:16] if a.source else None
+        src = sources_hash(a.source) if a.source else None
         out = {n: {k: v for k, v in r.items() if k != "counters"} for n, r in rep.items()}
         json.dump({"kernels": out, "command": a.command, "kernel_source_sha256_16": src},
                   open(a.json_out, "w"), indent=1)
@@ -114,7 +122,7 @@ def main():
         ap.add_argument("--counters", nargs="+", required=True)
         ap.add_argument("--command", required=True)
         ap.add_argument("--json-out", help="also write the derived shares as JSON")
-        ap.add_argument("--source", help="kernel source whose hash the JSON records")
+        ap.add_argument("--source", nargs="+", help="kernel sources whose hash the JSON records")
         main_counters(ap.parse_args())
         return
     ap = argparse.ArgumentParser()
@@ -124,6 +132,9 @@ def main():
     ap.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--command", required=True)
     ap.add_argument("--json-out")
+    ap.add_argument("--traffic-out", help="write the S2O attention kernel's traffic record (JSON) here")
+    ap.add_argument("--workload", default="", help="workload named in the traffic record")
+    ap.add_argument("--source", nargs="+", help="kernel sources whose hash the traffic record holds")
     a = ap.parse_args()
     print(f"command: {a.command}\n")
     print(f"{'kernel':44s} {'calls':>5s} {'avg ms':>10s} {'total ms':>10s} {'%':>6s}")
@@ -156,6 +167,17 @@ def main():
         print(f"{n:44s} {fb / 1e9:10.2f} {wb / 1e9:10.2f} {ms if ms else float('nan'):8.3f} {bw:8.0f}")
     if a.json_out:
         json.dump(out, open(a.json_out, "w"), indent=1)
+    if a.traffic_out:
+        k = out["s2o_attn_fwd (S2O schedule)"]
+        rec = {"kernel": "s2o_attn_fwd (attn_kernel_bf16<d=128, 4 waves, S2O>)", "workload": a.workload,
+               "fetch_bytes_per_launch": k["fetch_bytes"], "write_bytes_per_launch": k["write_bytes"],
+               "hbm_bytes_per_launch": k["fetch_bytes"] + k["write_bytes"], "avg_ms": k["avg_ms"],
+               "note": f"FETCH_SIZE x{fscale:.0f} and WRITE_SIZE x{wscale:.0f} (scales from a "
+                       "plain copy in the same run); these count every request that leaves L2, "
+                       "Infinity Cache hits included",
+               "command": a.command, "kernel_source_sha256_16": sources_hash(a.source) if a.source else None}
+        json.dump(rec, open(a.traffic_out, "w"), indent=1)
+        open(a.traffic_out, "a").write("\n")
 
 
 if __name__ == "__main__":

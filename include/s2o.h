@@ -42,6 +42,8 @@
  *     off(b, h, s) = (b*Hq + h)*L + S*s*(s-1)/2, and tile t uses list floor(t/P).
  *   Block lists: the same layouts with every length and history term divided
  *     by tile_n; idx values are block numbers in [0, a_t / tile_n).
+ *   Shared lists (S2O_SHARE_GQA): (b*Hkv + h/G) in place of (b*Hq + h), so the
+ *     G = Hq / Hkv query heads of a KV head use one list.
  *   Entries are int64-addressed; idx values are key positions in [0, a_t).
  */
 #ifndef S2O_H

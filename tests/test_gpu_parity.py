@@ -608,3 +608,20 @@ def test_llama8b_128k_shared_lists_sampled():
         say(f"oracle on {len(tiles)} sampled tiles")
         assert_report(compare(run, tiles, tau, o, ex, check_lists=(tau == 1.42e-3)), "bf16")
         del o, ex
+
+
+@pytest.mark.parametrize("share", [False, True], ids=["per_head", "shared"])
+def test_one_call_path_equals_the_three_calls(share):
+    """s2o_attention (problem from the tensors' shapes, score -> build_index ->
+    attention in one call) gives the explicit calls' outputs bit for bit."""
+    w = synth.custom_workload(B=2, Hq=4, Hkv=2, N=1024, d=128, dtype="bf16", tile_m=128, tile_n=64,
+                              seg_len=256, structure="stripes+band", n_stripes=10, seed=931, name="one_call")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, share_gqa=share)
+    o_ref, ex_ref = run.attn(1e-3)
+    say("s2o_attention")
+    o, ex = s2o.s2o_attention(run.q, run.k, run.v, 1e-3, w.seg_len, tile=(w.tile_m, w.tile_n), scale=w.scale,
+                              share_gqa=share)
+    torch.cuda.synchronize()
+    assert torch.equal(ex.view(-1), ex_ref.view(-1))
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))

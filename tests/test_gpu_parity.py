@@ -625,3 +625,17 @@ def test_one_call_path_equals_the_three_calls(share):
     torch.cuda.synchronize()
     assert torch.equal(ex.view(-1), ex_ref.view(-1))
     assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("lists", ["segment", "tile_blocks"])
+def test_llama8b_16k_shared_segment_and_block_lists(lists):
+    w = synth.WORKLOADS["llama8b_n16k"]
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists=lists, share_gqa=True)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    tiles = sample_tiles(w, heads=(2, 13, 31), n_random=12, seed=17)
+    for tau in (1e-2, 1e-3):
+        o, ex = run.attn(tau)
+        assert_report(compare(run, tiles, tau, o, ex), "bf16")

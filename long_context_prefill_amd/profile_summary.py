@@ -94,6 +94,65 @@ def counter_report(paths):
     return out
 
 
+# MI355X has 256 CUs; a wave64 vector instruction holds its SIMD for 4 cycles
+# at full rate (transcendentals take longer, so the busy share below is a floor).
+CUS = 256
+
+
+def kernel_counter_table(paths, kernels):
+    """Per-dispatch SQ counter averages of the named kernels (short names) and
+    the shares derived from them: vector unit busy (SQ_INSTS_VALU x 4 cycles
+    over SIMD cycles), LDS busy (SQ_LDS_IDX_ACTIVE per CU over SE busy
+    cycles), bank-conflict share of LDS-active cycles, and the wave-time
+    split.  A share is left out when its counters were not collected."""
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            n = short(r["Kernel_Name"])
+            if n in kernels:
+                per[n][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = {}
+    for n in kernels:
+        if n not in per:
+            continue
+        avg = {c: sum(v) / len(v) for c, v in per[n].items()}
+        d = {"counters": avg}
+        if "SQ_BUSY_CYCLES" in avg:
+            se = avg["SQ_BUSY_CYCLES"] / SHADER_ENGINES
+            if "SQ_INSTS_VALU" in avg:
+                d["valu_busy"] = avg["SQ_INSTS_VALU"] * 4 / (se * SIMDS)
+            if "SQ_LDS_IDX_ACTIVE" in avg:
+                d["lds_busy"] = avg["SQ_LDS_IDX_ACTIVE"] / CUS / se
+        if "SQ_LDS_IDX_ACTIVE" in avg and "SQ_LDS_BANK_CONFLICT" in avg and avg["SQ_LDS_IDX_ACTIVE"] > 0:
+            d["lds_bank_conflict_share"] = avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"]
+        if all(c in avg for c in ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY")):
+            w = avg["SQ_WAVE_CYCLES"]
+            d["wave_issuing"] = avg["SQ_ACTIVE_INST_ANY"] / w
+            d["wave_waiting_issue"] = avg["SQ_WAIT_INST_ANY"] / w
+            d["wave_waiting_counters_barrier"] = avg["SQ_WAIT_ANY"] / w
+        out[n] = d
+    return out
+
+
+def main_kernel_counters(a):
+    print(f"command: {a.command}\n")
+    for n, d in kernel_counter_table(a.counters, a.kernels).items():
+        print(f"{n}: per dispatch")
+        for c, v in sorted(d["counters"].items()):
+            print(f"  {c:32s} {v:14.4g}")
+        if "valu_busy" in d:
+            print(f"  vector unit busy (full-rate floor) {100 * d['valu_busy']:6.1f} % of SIMD cycles")
+        if "lds_busy" in d:
+            print(f"  LDS busy                           {100 * d['lds_busy']:6.1f} % of CU cycles")
+        if "lds_bank_conflict_share" in d:
+            print(f"  bank conflicts                     {100 * d['lds_bank_conflict_share']:6.1f} % of LDS-active cycles")
+        if "wave_issuing" in d:
+            print(f"  wave time issuing / waiting for an issue slot / at waits and barriers: "
+                  f"{100 * d['wave_issuing']:.0f} / {100 * d['wave_waiting_issue']:.0f} / "
+                  f"{100 * d['wave_waiting_counters_barrier']:.0f} %")
+        print()
+
+
 def main_counters(a):
     print(f"command: {a.command}\n")
     rep = counter_report(a.counters)
@@ -123,7 +182,12 @@ def main():
         ap.add_argument("--command", required=True)
         ap.add_argument("--json-out", help="also write the derived shares as JSON")
         ap.add_argument("--source", nargs="+", help="kernel sources whose hash the JSON records")
-        main_counters(ap.parse_args())
+        ap.add_argument("--kernels", nargs="+", help="short kernel names: a generic table for these")
+        a = ap.parse_args()
+        if a.kernels:
+            main_kernel_counters(a)
+        else:
+            main_counters(a)
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("stats")

@@ -178,8 +178,18 @@ __global__ __launch_bounds__(THREADS) void minmax_kernel(const float *__restrict
     __shared__ float red[2][NWAVES];
     const float *s = scores + (int64_t)blockIdx.x * E;
     float lo = INFINITY, hi = -INFINITY;
-    for (int i = 4 * threadIdx.x; i < E; i += 4 * THREADS) {
-        const float4 x = *reinterpret_cast<const float4 *>(s + i);
+    // every load of the thread is issued before the first is used
+    constexpr int PER = MAX_BLOCK / (4 * THREADS);
+    float4 xs[PER];
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int i = 4 * threadIdx.x + it * 4 * THREADS;
+        if (i < E) xs[it] = *reinterpret_cast<const float4 *>(s + i);
+    }
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        if (4 * threadIdx.x + it * 4 * THREADS >= E) break;
+        const float4 x = xs[it];
         lo = fminf(fminf(lo, x.x), fminf(x.y, fminf(x.z, x.w)));
         hi = fmaxf(fmaxf(hi, x.x), fmaxf(x.y, fmaxf(x.z, x.w)));
     }
@@ -215,8 +225,17 @@ __global__ __launch_bounds__(THREADS) void hist_kernel(const float *__restrict__
     const Buckets bk = list_buckets(g, blk_list, blk_mm, E, sh);  // synchronises
     const int wave = threadIdx.x >> 6;
     const float *s = scores + (int64_t)blockIdx.x * E;
-    for (int i = 4 * threadIdx.x; i < E; i += 4 * THREADS) {
-        const float4 x = *reinterpret_cast<const float4 *>(s + i);
+    constexpr int PER = MAX_BLOCK / (4 * THREADS);
+    float4 xs[PER];  // every load of the thread is issued before the first is used
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        const int i = 4 * threadIdx.x + it * 4 * THREADS;
+        if (i < E) xs[it] = *reinterpret_cast<const float4 *>(s + i);
+    }
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+        if (4 * threadIdx.x + it * 4 * THREADS >= E) break;
+        const float4 x = xs[it];
         atomicAdd(&cnt[wave][bucket_digit(x.x, bk)], 1);
         atomicAdd(&cnt[wave][bucket_digit(x.y, bk)], 1);
         atomicAdd(&cnt[wave][bucket_digit(x.z, bk)], 1);

@@ -151,7 +151,8 @@ size_t s2o_score_workspace_bytes(const s2o_problem *p);
  * representative query; only causal-prefix keys count).  For every list with
  * history: qbar = the tile's mean query (fp32 sum over its BM rows in ascending
  * order, then an exact scaling by 1/BM) or, for per-segment lists, the
- * segment's representative described above; then
+ * segment's representative described above (with S2O_SHARE_GQA, the mean of
+ * the group's G such representatives); then
  *   scores[off + j] = fp32 fma chain over k = 0..d-1 of qbar[k] * K[b, h/G, j, k],
  * accumulated from 0 in ascending k, for j in [0, history length).  This order
  * is part of the definition, so results are bit-reproducible.

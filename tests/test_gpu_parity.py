@@ -99,10 +99,17 @@ def test_small_bf16_every_tile(case):
     scores_o = oracle.scores_all(run.po, x["q"], x["k"])
     assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
     assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
-    for tau in (0.0, 1e-3, 3e-2, 0.3):
+    for tau in (0.0, 1e-3, 3e-2, 0.3, 1.0):
         o, ex = run.attn(tau)
         rep = compare(run, all_tiles(w), tau, o, ex, check_lists=False)
         assert_report(rep, "bf16")
+    # tau >= 1: no chunk can gain that much, so every tile with history runs
+    # pass 1 and exactly its first list chunk
+    ex = ex.cpu().numpy()
+    for (b, h, t) in all_tiles(w):
+        a = t * BM // S * S
+        p1 = ((t + 1) * BM - a + 63) // 64
+        assert ex[b, h, t] == p1 + (1 if a > 0 else 0), (b, h, t)
 
 
 def test_large_logit_jump_restarts_with_running_max():

@@ -646,3 +646,28 @@ def test_llama8b_16k_shared_segment_and_block_lists(lists):
     for tau in (1e-2, 1e-3):
         o, ex = run.attn(tau)
         assert_report(compare(run, tiles, tau, o, ex), "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_llama8b_64k_lists_of_three_heads_and_sampled_attention():
+    """The 64K workload (S = 8192, tau = 1e-3): every list of three query heads
+    bit for bit against the oracle, and attention on sampled tiles."""
+    w = synth.WORKLOADS["llama8b_n64k"]
+    say("generating llama8b_n64k inputs")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x)
+    scores = run.scores.cpu().numpy()
+    idx = run.idx.cpu().numpy()
+    for h in (0, 13, 31):
+        say(f"oracle lists of head {h}")
+        for t in range(w.N // w.tile_m):
+            a = oracle.list_len(run.po, t)
+            if a == 0:
+                continue
+            off = s2o.list_offset(run.p, 0, h, t)
+            sc = oracle.score_tile(run.po, x["q"], x["k"], 0, h, t)
+            assert np.array_equal(scores[off:off + a].view(np.uint32), sc.view(np.uint32)), (h, t)
+            assert np.array_equal(idx[off:off + a], oracle.order(sc)), (h, t)
+    tiles = sample_tiles(w, heads=(0, 13, 31), n_random=8, seed=29)
+    o, ex = run.attn(1e-3)
+    assert_report(compare(run, tiles, 1e-3, o, ex), "bf16")

@@ -261,18 +261,32 @@ __global__ __launch_bounds__(NB) void scan_kernel(int32_t *__restrict__ hist, in
     if (L.len == 0) return;
     const int64_t b0 = L.off / E, nb = L.len / E;
     const int v = threadIdx.x;
+    // the blocks' counts are read SCAN_BATCH at a time, all loads before the first use
+    constexpr int SCAN_BATCH = 8;
     int run = 0;
-    for (int64_t bb = b0; bb < b0 + nb; ++bb) {
-        const int c = hist[bb * NB + v];
-        hist[bb * NB + v] = run;
-        run += c;
+    for (int64_t bb = b0; bb < b0 + nb; bb += SCAN_BATCH) {
+        int c[SCAN_BATCH];
+#pragma unroll
+        for (int u = 0; u < SCAN_BATCH; ++u) c[u] = bb + u < b0 + nb ? hist[(bb + u) * NB + v] : 0;
+#pragma unroll
+        for (int u = 0; u < SCAN_BATCH; ++u) {
+            if (bb + u < b0 + nb) hist[(bb + u) * NB + v] = run;
+            run += c[u];
+        }
     }
     tot[v] = run;
     __syncthreads();
     scan256(tot);
     __syncthreads();
     const int base = tot[v];
-    for (int64_t bb = b0; bb < b0 + nb; ++bb) hist[bb * NB + v] += (int)(base + L.off - bb * E);
+    for (int64_t bb = b0; bb < b0 + nb; bb += SCAN_BATCH) {
+        int c[SCAN_BATCH];
+#pragma unroll
+        for (int u = 0; u < SCAN_BATCH; ++u) c[u] = bb + u < b0 + nb ? hist[(bb + u) * NB + v] : 0;
+#pragma unroll
+        for (int u = 0; u < SCAN_BATCH; ++u)
+            if (bb + u < b0 + nb) hist[(bb + u) * NB + v] = c[u] + (int)(base + L.off - (bb + u) * E);
+    }
     int32_t *bs = bstart + (int64_t)blockIdx.x * (NB + 1);
     bs[v] = base;
     if (v == 0) bs[NB] = (int32_t)L.len;

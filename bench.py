@@ -31,7 +31,9 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -112,6 +114,8 @@ def parse():
     ap.add_argument("--modes", default="segment,tile_blocks,tile+qperm,tile+gqa",
                     help="list forms measured besides the headline per-tile lists")
     ap.add_argument("--no-ranking-study", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip sampling the GPU clock and power while the attention kernel repeats")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration for profiles)")
     return ap.parse_args()
@@ -152,6 +156,56 @@ def mfma_busy_counter():
         return None
     k = rec.get("kernels", {}).get("s2o_attn_fwd (S2O schedule)")
     return round(k["mfma_busy"], 4) if k else None
+
+
+def amd_smi_sample():
+    """One reading: mean gfx clock over the XCDs (MHz) and socket power (W), or None."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "-p", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        g = json.loads(r.stdout)["gpu_data"][0]
+        clks = [float(v["clk"]["value"]) for k, v in g["clock"].items() if k.startswith("gfx_")]
+        return sum(clks) / len(clks), float(g["power"]["socket_power"]["value"])
+    except Exception:  # tool missing, busy or in another format: no reading
+        return None
+
+
+def clocks_under_load(launch, seconds=6.0):
+    """Samples amd-smi from a second thread while `launch()` (one kernel launch)
+    repeats on the GPU for about `seconds`, after the timed steps.  None when no
+    reading was possible (or when run under a profiler, whose preload every
+    child process would inherit)."""
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        return None
+    import torch
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            s = amd_smi_sample()
+            if s is None:
+                return
+            samples.append(s)
+
+    for _ in range(3):  # reach a steady clock first
+        launch()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds and th.is_alive():
+        launch()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=60)
+    if not samples:
+        return None
+    clk, pw = [c for c, _ in samples], [w for _, w in samples]
+    return {"gfx_mhz_mean": round(sum(clk) / len(clk)), "gfx_mhz_min": round(min(clk)),
+            "gfx_mhz_max": round(max(clk)), "socket_power_w_mean": round(sum(pw) / len(pw)),
+            "socket_power_w_max": round(max(pw)), "samples": len(samples),
+            "source": "amd-smi metric -c -p while s2o_attn_fwd repeats (headline lists and tau), "
+                      "after the timed steps"}
 
 
 def gather_figure(attn_ms):
@@ -378,6 +432,10 @@ def main():
                       "p90": round(float(np.percentile(step, 90)), 3)}
         executed = int(exec_tiles.sum())
         achieved = executed * flop_per_tile / (attn_ms * 1e-3) / 1e12
+        clocks = None
+        if mode == "tile" and not args.no_clocks:
+            log(f"[{mode}] sampling clocks and power while the attention kernel repeats")
+            clocks = clocks_under_load(lambda: s2o.s2o_attn_fwd(p, q, k, v, idx, tau, out, exec_tiles))
         study = None
         if not args.no_ranking_study:
             log(f"[{mode}] ranking study on {len(study_tiles)} tiles")
@@ -394,7 +452,7 @@ def main():
         log(f"[{mode}] step {ms_per_step:.2f} ms = score {score_ms:.2f} + build_index "
             f"{sort_ms:.2f} + attn {attn_ms:.2f}")
         res = {"tau": tau, "ms_per_step": ms_per_step, "score_ms": score_ms, "sort_ms": sort_ms,
-               "attn_ms": attn_ms, "step_stats": step_stats, "executed": executed, "density": executed / dense_tiles,
+               "attn_ms": attn_ms, "step_stats": step_stats, "clocks": clocks, "executed": executed, "density": executed / dense_tiles,
                "mse": chosen["mse"], "rel_mse": chosen["rel_mse"], "achieved": achieved,
                "sweep": sweep, "exec_tiles": exec_tiles.cpu().numpy(), "study": study}
         del scores, idx, ws_score, ws_sort, out, exec_tiles
@@ -447,6 +505,7 @@ def main():
                      "traffic": traffic_figure(), "kernel": "s2o_attn_fwd",
                      "work": f"{main['executed']} executed 128x64 tiles x {flop_per_tile:.0f} flop"},
         "gathers": gather_figure(main["attn_ms"]),
+        "clocks_during_attention": main["clocks"],
     }
     names = {"segment": "segment_lists", "tile_blocks": "block_lists",
              "segment_blocks": "segment_block_lists", "tile+qperm": "query_permutation",

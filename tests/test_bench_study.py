@@ -153,3 +153,30 @@ def test_by_tau_precision_and_recall_follow_the_definitions():
 def test_study_without_taus_has_no_table():
     r = _run(lambda o, a, bn: o, n_chunks=2)
     assert "by_tau" not in r
+
+
+def test_amd_smi_sample_parses_clocks_and_power(monkeypatch):
+    import json
+    import subprocess
+    out = {"gpu_data": [{"gpu": 0, "power": {"socket_power": {"value": 900, "unit": "W"}},
+                         "clock": {**{f"gfx_{i}": {"clk": {"value": 1600 + 10 * i, "unit": "MHz"}} for i in range(8)},
+                                   "mem_0": {"clk": {"value": 1900, "unit": "MHz"}}}}]}
+
+    class R:
+        stdout = json.dumps(out)
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: R())
+    clk, pw = bench.amd_smi_sample()
+    assert clk == 1635.0 and pw == 900.0  # mean of the gfx clocks only
+
+
+def test_clocks_under_load_summarises_samples(monkeypatch):
+    readings = iter([(1600.0, 800.0), (1700.0, 1000.0)])
+    monkeypatch.setattr(bench, "amd_smi_sample", lambda: next(readings, None))
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+    monkeypatch.delenv("LD_PRELOAD", raising=False)
+    r = bench.clocks_under_load(lambda: None, seconds=0.2)
+    assert r["samples"] == 2 and r["gfx_mhz_mean"] == 1650 and r["gfx_mhz_min"] == 1600
+    assert r["socket_power_w_mean"] == 900 and r["socket_power_w_max"] == 1000
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/librocprofiler-sdk-tool.so")
+    assert bench.clocks_under_load(lambda: None, seconds=0.2) is None

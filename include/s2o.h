@@ -79,7 +79,8 @@ typedef struct {
     int32_t seg_len;  /* S > 0, multiple of tile_m; N need not be a multiple of S */
     int32_t tile_m;   /* BM: 64 or 128 */
     int32_t tile_n;   /* BN: 64 */
-    float scale;      /* softmax scale (1/sqrt(d) for standard attention), finite */
+    float scale;      /* softmax scale (1/sqrt(d) for standard attention): finite and > 0,
+                         else S2O_ERR_INVALID_ARG */
     int32_t list_granularity; /* one of the S2O_LISTS_* values below, optionally ORed with
                                  S2O_QUERY_PERMUTATION or S2O_SHARE_GQA */
 } s2o_problem;

@@ -28,7 +28,9 @@ s2o_status make_geometry(const s2o_problem *p, Geometry &g) {
         return S2O_ERR_INVALID_ARG;
     if (p->dtype != S2O_F32 && p->dtype != S2O_BF16) return S2O_ERR_INVALID_ARG;
     if (p->causal != 0 && p->causal != 1) return S2O_ERR_INVALID_ARG;
-    if (!isfinite(p->scale)) return S2O_ERR_INVALID_ARG;
+    // the kernels mask with -inf before scaling and take row maxima on raw
+    // logits, which needs a positive scale
+    if (!isfinite(p->scale) || !(p->scale > 0.0f)) return S2O_ERR_INVALID_ARG;
     if (p->heads_q % p->heads_kv != 0) return S2O_ERR_INVALID_ARG;
     if (p->tile_m % p->tile_n != 0 || p->seq_len % p->tile_m != 0 || p->seg_len % p->tile_m != 0)
         return S2O_ERR_INVALID_ARG;

@@ -24,9 +24,8 @@
 //     LDS and the PV operand is read with the transposing ds_read_b64_tr_b16;
 //     the softmax reference is fixed after a tile's first chunk, with a
 //     running-max restart when a chunk's mass overflows the check;
-//   * fp32 (attn_kernel_staged): rows are staged through registers, V is
-//     written to LDS transposed (keys innermost) so the PV operand reads are
-//     contiguous;
+//   * fp32 (attn_kernel_f32): rows are staged through registers into
+//     row-major LDS tiles, with the lazy running max throughout;
 //   * the stop decision is uniform per workgroup: each wave ballots whether
 //     any of its rows still gains >= tau, the waves exchange one flag each
 //     through LDS at the barrier that already separates the LDS buffers;
@@ -34,6 +33,7 @@
 //     sharing one KV head are placed on the same XCD so they share its L2.
 #include "s2o_internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace s2o {
@@ -116,12 +116,10 @@ __device__ inline void mask_chunk(f32x16 &s0, f32x16 &s1, int key0, int row, int
     }
 }
 
-// Online-softmax update of one chunk for this lane's row.  Turns s0/s1 into
-// probabilities exp2(s*c - m); returns the chunk mass delta and the rescale
-// factor of the old state.  The running max m is only moved when the chunk's
-// max exceeds it by more than kMaxSlack (log2 units): probabilities then stay
-// below 2^kMaxSlack, and since l, delta and acc all use the same m the result
-// (acc / l, delta / l) is unchanged while most chunks skip the rescale.
+// The running max m is only moved when a chunk's max exceeds it by more than
+// kMaxSlack (log2 units): probabilities then stay below 2^kMaxSlack, and since
+// l, delta and acc all use the same m the result (acc / l, delta / l) is
+// unchanged while most chunks skip the rescale.
 constexpr float kMaxSlack = 8.0f;
 // Headroom (log2 units) between chunk 0's row max and the fixed reference of
 // the bf16 kernel's first attempt: later logits may exceed that max by up to
@@ -129,25 +127,6 @@ constexpr float kMaxSlack = 8.0f;
 // than 126 - kFastHeadroom below it underflow, negligible against the row's
 // chunk-0 mass (>= 2^-kFastHeadroom).
 constexpr float kFastHeadroom = 60.0f;
-
-__device__ inline void softmax_chunk(f32x16 &s0, f32x16 &s1, float c, float &m, float &l,
-                                     float &alpha, float &delta) {
-    float mx = pair_max(fmaxf(max16(s0), max16(s1))) * c;
-    float m_new = mx > m + kMaxSlack ? mx : m;
-    alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 on the first chunk (m = -inf)
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
-        s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum += s0[r] + s1[r];
-    sum = pair_sum(sum);
-    delta = sum;
-    l = l * alpha + sum;
-    m = m_new;
-}
 
 template <int NACC>
 __device__ inline void rescale(f32x16 (&acc)[NACC], float alpha) {
@@ -159,46 +138,32 @@ __device__ inline void rescale(f32x16 (&acc)[NACC], float alpha) {
         for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
 }
 
-__device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-// Position of chunk key j (0..63) inside a transposed-V row: within each group
-// of 16 keys, j = 8q + 4h + e is stored at 8h + 4q + e, so the 8 keys a lane
-// half feeds to one MFMA step are contiguous.
-__device__ inline int vpos(int j) {
-    return (j & ~15) | ((j & 4) << 1) | ((j & 8) >> 1) | (j & 3);
-}
-
-template <typename T, int D, int NW, bool S2O>
-struct Cfg {
-    static constexpr bool kBf16 = sizeof(T) == 2;
+// fp32 kernel (attn_kernel_f32): fp32 MFMA (v_mfma_f32_32x32x2_f32), K and V
+// rows staged through registers into row-major LDS tiles (rows padded so the
+// operand reads are conflict-free), the same two-stage pipeline and stop
+// decision as the bf16 kernel, and the lazy running max throughout.
+template <int D, int NW>
+struct FCfg {
     static constexpr int BM = 32 * NW;
     static constexpr int NT = 64 * NW;
     static constexpr int BN = kTileN;
-    // LDS row strides in elements (padding chosen for conflict-free MFMA
-    // operand reads and transposed writes)
-    static constexpr int KSTR = kBf16 ? D + 8 : D + 2;
-    static constexpr int VROWS = kBf16 ? D : BN;           // V^T rows (bf16) or V rows (fp32)
-    static constexpr int VSTR = kBf16 ? BN + 4 : D + 8;
+    static constexpr int KSTR = D + 2;                      // K row stride (floats)
+    static constexpr int VSTR = D + 8;                      // V row stride (floats)
     static constexpr int KBUF = BN * KSTR;
-    static constexpr int VBUF = VROWS * VSTR;
-    static constexpr int BUF = KBUF + VBUF;                 // elements per stage
-    static constexpr size_t LDS_BYTES = 2 * BUF * sizeof(T);
-    // global -> register staging
-    static constexpr int EPV = 16 / sizeof(T);              // elements per 16-byte piece
-    static constexpr int KPIECES = BN * D / EPV / NT;       // K pieces per thread
-    // bf16: V is loaded as row pairs (two 16-byte pieces) and transposed;
-    // fp32: V is loaded like K.
-    static constexpr int VITEMS = kBf16 ? (BN / 2) * (D / 8) / NT : KPIECES;
-    static_assert(KPIECES >= 1 && VITEMS >= 1, "tile too small for the thread count");
+    static constexpr int VBUF = BN * VSTR;
+    static constexpr int BUF = KBUF + VBUF;                 // floats per stage
+    static constexpr size_t LDS_BYTES = 2 * BUF * sizeof(float);
+    static constexpr int KCG = D / 4;                       // 16-byte pieces per row
+    static constexpr int PIECES = BN * KCG / NT;            // pieces per thread per tile
+    static_assert(PIECES >= 1, "tile too small for the thread count");
 };
 
-template <typename T, int D, int NW, bool S2O>
-__global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel_staged(AttnParams a) {
-    using C = Cfg<T, D, NW, S2O>;
+template <int D, int NW, bool S2O>
+__global__ __launch_bounds__(64 * NW, 1) void attn_kernel_f32(AttnParams a) {
+    using C = FCfg<D, NW>;
     constexpr int BM = C::BM, NT = C::NT, BN = C::BN;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    T *lds = reinterpret_cast<T *>(smem_raw);
+    float *lds = reinterpret_cast<float *>(smem_raw);
     __shared__ int flags[2][NW];
 
     const Geometry &g = a.g;
@@ -220,103 +185,51 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
     const int32_t *list = S2O ? a.idx + list_offset(g, b, h, t) : nullptr;
 
     const int kvh = h / g.G;
-    const T *Qp = reinterpret_cast<const T *>(a.q) + ((int64_t)(b * g.Hq + h) * g.N) * D;
-    const T *Kp = reinterpret_cast<const T *>(a.k) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
-    const T *Vp = reinterpret_cast<const T *>(a.v) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
+    const float *Qp = reinterpret_cast<const float *>(a.q) + ((int64_t)(b * g.Hq + h) * g.N) * D;
+    const float *Kp = reinterpret_cast<const float *>(a.k) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
+    const float *Vp = reinterpret_cast<const float *>(a.v) + ((int64_t)(b * g.Hkv + kvh) * g.N) * D;
 
     auto chunk_row = [&](int k, int p) -> int {
         if (k < n1) return base1 + k * BN + p;
         return g.blocks ? list[k - n1] * BN + p : list[(k - n1) * BN + p];
     };
 
-    // ---- per-thread staging geometry
-    constexpr int KCG = D / C::EPV;  // 16-byte pieces per row
-    int krow_p[C::KPIECES], kcg[C::KPIECES];
+    // per-thread staging: piece i of a tile is row (i*NT + tid) / KCG, column
+    // group (i*NT + tid) % KCG, for K and V alike
+    int prow[C::PIECES], pcg[C::PIECES], rows[C::PIECES];
 #pragma unroll
-    for (int i = 0; i < C::KPIECES; ++i) {
-        int pc = i * NT + tid;
-        krow_p[i] = pc / KCG;
-        kcg[i] = pc % KCG;
+    for (int i = 0; i < C::PIECES; ++i) {
+        prow[i] = (i * NT + tid) / C::KCG;
+        pcg[i] = (i * NT + tid) % C::KCG;
     }
-    int vrow_p[C::VITEMS], vcg[C::VITEMS];
-#pragma unroll
-    for (int i = 0; i < C::VITEMS; ++i) {
-        int I = i * NT + tid;
-        if constexpr (C::kBf16) {
-            vrow_p[i] = 2 * ((I >> 2) & 31);       // first row of the pair
-            vcg[i] = 4 * (I >> 7) + (I & 3);       // 8-column group
-        } else {
-            vrow_p[i] = I / KCG;
-            vcg[i] = I % KCG;
-        }
-    }
-    int krow[C::KPIECES], vrow[C::VITEMS][2];
-    u32x4 kreg[C::KPIECES], vreg[C::VITEMS][2];
-
+    u32x4 kreg[C::PIECES], vreg[C::PIECES];
     auto fetch_rows = [&](int k) {
 #pragma unroll
-        for (int i = 0; i < C::KPIECES; ++i) krow[i] = chunk_row(k, krow_p[i]);
-#pragma unroll
-        for (int i = 0; i < C::VITEMS; ++i) {
-            vrow[i][0] = chunk_row(k, vrow_p[i]);
-            if constexpr (C::kBf16) vrow[i][1] = chunk_row(k, vrow_p[i] + 1);
-        }
+        for (int i = 0; i < C::PIECES; ++i) rows[i] = chunk_row(k, prow[i]);
     };
     auto issue_loads = [&]() {
 #pragma unroll
-        for (int i = 0; i < C::KPIECES; ++i)
-            kreg[i] = *reinterpret_cast<const u32x4 *>(Kp + (int64_t)krow[i] * D + kcg[i] * C::EPV);
-#pragma unroll
-        for (int i = 0; i < C::VITEMS; ++i) {
-            vreg[i][0] = *reinterpret_cast<const u32x4 *>(Vp + (int64_t)vrow[i][0] * D + vcg[i] * C::EPV);
-            if constexpr (C::kBf16)
-                vreg[i][1] = *reinterpret_cast<const u32x4 *>(Vp + (int64_t)vrow[i][1] * D + vcg[i] * 8);
+        for (int i = 0; i < C::PIECES; ++i) {
+            kreg[i] = *reinterpret_cast<const u32x4 *>(Kp + (int64_t)rows[i] * D + pcg[i] * 4);
+            vreg[i] = *reinterpret_cast<const u32x4 *>(Vp + (int64_t)rows[i] * D + pcg[i] * 4);
         }
     };
     auto store_lds = [&](int buf) {
-        T *Kl = lds + buf * C::BUF;
-        T *Vl = Kl + C::KBUF;
+        float *Kl = lds + buf * C::BUF;
+        float *Vl = Kl + C::KBUF;
 #pragma unroll
-        for (int i = 0; i < C::KPIECES; ++i) {
-            T *dst = Kl + krow_p[i] * C::KSTR + kcg[i] * C::EPV;
-            if constexpr (C::kBf16) {
-                *reinterpret_cast<u32x4 *>(dst) = kreg[i];
-            } else {  // fp32 rows are only 8-byte aligned
-                reinterpret_cast<u32x2 *>(dst)[0] = kreg[i].xy;
-                reinterpret_cast<u32x2 *>(dst)[1] = kreg[i].zw;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < C::VITEMS; ++i) {
-            if constexpr (C::kBf16) {
-                // transpose a 2x8 block: V[j][c], V[j+1][c] -> V^T[c][vpos(j)] (4 bytes)
-                const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-                const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-                uint16_t *Vt = reinterpret_cast<uint16_t *>(Vl);
-                int pos = vpos(vrow_p[i]);
-                int c0 = vcg[i] * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    uint32_t pk = (e & 1) ? pack_hi(w0[e >> 1], w1[e >> 1]) : pack_lo(w0[e >> 1], w1[e >> 1]);
-                    *reinterpret_cast<uint32_t *>(Vt + (c0 + e) * C::VSTR + pos) = pk;
-                }
-            } else {
-                *reinterpret_cast<u32x4 *>(Vl + vrow_p[i] * C::VSTR + vcg[i] * 4) = vreg[i][0];
-            }
+        for (int i = 0; i < C::PIECES; ++i) {
+            float *dst = Kl + prow[i] * C::KSTR + pcg[i] * 4;  // K rows are only 8-byte aligned
+            reinterpret_cast<u32x2 *>(dst)[0] = kreg[i].xy;
+            reinterpret_cast<u32x2 *>(dst)[1] = kreg[i].zw;
+            *reinterpret_cast<u32x4 *>(Vl + prow[i] * C::VSTR + pcg[i] * 4) = vreg[i];
         }
     };
 
-    // ---- Q operand in registers (B operand of S^T = K Q^T)
-    constexpr int QSTEPS = C::kBf16 ? D / 16 : D / 2;
-    using QReg = typename std::conditional<C::kBf16, bf16x8, float>::type;
-    QReg qf[QSTEPS];
+    // Q operand in registers (B operand of S^T = K Q^T)
+    float qf[D / 2];
 #pragma unroll
-    for (int s = 0; s < QSTEPS; ++s) {
-        if constexpr (C::kBf16)
-            qf[s] = *reinterpret_cast<const bf16x8 *>(Qp + (int64_t)my_row * D + 16 * s + 8 * half);
-        else
-            qf[s] = Qp[(int64_t)my_row * D + 2 * s + half];
-    }
+    for (int s = 0; s < D / 2; ++s) qf[s] = Qp[(int64_t)my_row * D + 2 * s + half];
 
     constexpr int NACC = D / 32;
     f32x16 acc[NACC];
@@ -327,73 +240,41 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
     float m = -INFINITY, l = 0.f;
     const float c = a.scale_log2;
 
-    // QK^T of the chunk in stage `buf`: s0/s1 = keys 0..31 / 32..63 of the
-    // chunk against this lane's query row
+    // S^T of the chunk in stage `buf`: s0/s1 = keys 0..31 / 32..63 of the chunk
+    // against this lane's query row
     auto qk = [&](int buf, f32x16 &s0, f32x16 &s1) {
-        const T *Kl = lds + buf * C::BUF;
+        const float *Kl = lds + buf * C::BUF;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s0[r] = s1[r] = 0.f;
-        if constexpr (C::kBf16) {
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                bf16x8 ka = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 16 * s + 8 * half);
-                bf16x8 kb = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 16 * s + 8 * half);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s], s1, 0, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int s = 0; s < D / 2; ++s) {
-                float ka = Kl[li * C::KSTR + 2 * s + half];
-                float kb = Kl[(32 + li) * C::KSTR + 2 * s + half];
-                s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kb, qf[s], s1, 0, 0, 0);
-            }
+        for (int s = 0; s < D / 2; ++s) {
+            float ka = Kl[li * C::KSTR + 2 * s + half];
+            float kb = Kl[(32 + li) * C::KSTR + 2 * s + half];
+            s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf[s], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kb, qf[s], s1, 0, 0, 0);
         }
     };
-    // O^T += V^T P^T with the probabilities of the chunk in stage `buf`
+    // O^T += V^T P^T with the probabilities of the chunk in stage `buf`; register r
+    // of block 0 / 1 is key 8*(r/4) + 4*half + r%4 (+32) of the chunk
     auto pv = [&](int buf, const f32x16 &p0, const f32x16 &p1) {
-        const T *Vl = lds + buf * C::BUF + C::KBUF;
-        if constexpr (C::kBf16) {
-            bf16x8 pb[4];
+        const float *Vl = lds + buf * C::BUF + C::KBUF;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[0][e] = (__bf16)p0[e];
-                pb[1][e] = (__bf16)p0[8 + e];
-                pb[2][e] = (__bf16)p1[e];
-                pb[3][e] = (__bf16)p1[8 + e];
-            }
-            const uint16_t *Vt = reinterpret_cast<const uint16_t *>(Vl);
+        for (int cb = 0; cb < NACC; ++cb) {
 #pragma unroll
-            for (int cb = 0; cb < NACC; ++cb) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const uint16_t *src = Vt + (32 * cb + li) * C::VSTR + 16 * s + 8 * half;
-                    u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
-                    u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 4);
-                    bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int cb = 0; cb < NACC; ++cb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    int j = 8 * (r >> 2) + 4 * half + (r & 3);
-                    float v0 = Vl[j * C::VSTR + 32 * cb + li];
-                    float v1 = Vl[(32 + j) * C::VSTR + 32 * cb + li];
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, p0[r], acc[cb], 0, 0, 0);
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, p1[r], acc[cb], 0, 0, 0);
-                }
+            for (int r = 0; r < 16; ++r) {
+                int j = 8 * (r >> 2) + 4 * half + (r & 3);
+                float v0 = Vl[j * C::VSTR + 32 * cb + li];
+                float v1 = Vl[(32 + j) * C::VSTR + 32 * cb + li];
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v0, p0[r], acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v1, p1[r], acc[cb], 0, 0, 0);
             }
         }
     };
 
     // Software pipeline.  During iteration k the LDS stages hold chunks k and
-    // k+1 and the registers receive chunk k+2; the matrix cores compute
-    // S_{k+1} = K_{k+1} Q^T while the vector ALUs run the softmax of chunk k,
-    // then PV(k) accumulates.  After a stop the speculative S_{k+1} is dropped.
+    // k+1 and the registers receive chunk k+2; S_{k+1} = K_{k+1} Q^T is computed
+    // before the softmax of chunk k, then PV(k) accumulates.  After a stop the
+    // speculative S_{k+1} is dropped.
     fetch_rows(0);
     issue_loads();
     store_lds(0);
@@ -425,76 +306,18 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         m = m_new;
 
-        // phase 1: S_{k+1} = K_{k+1} Q^T on the matrix cores, interleaved with
-        // the exponentials of chunk k (stale data when k+1 == total; unused then)
         f32x16 sn0, sn1;
+        qk(buf ^ 1, sn0, sn1);  // stale stage when k+1 == total; unused then
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sn0[r] = sn1[r] = 0.f;
-        if constexpr (C::kBf16) {
-            const T *Kl = lds + (buf ^ 1) * C::BUF;
-            constexpr int STEPS = D / 16;
-            constexpr int EPS = 16 / STEPS;  // exponentials per block per step
-            bf16x8 ka[2], kb[2];
-            ka[0] = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 8 * half);
-            kb[0] = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 8 * half);
-#pragma unroll
-            for (int st = 0; st < STEPS; ++st) {
-                if (st + 1 < STEPS) {
-                    ka[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kl + li * C::KSTR + 16 * (st + 1) + 8 * half);
-                    kb[(st + 1) & 1] = *reinterpret_cast<const bf16x8 *>(Kl + (32 + li) * C::KSTR + 16 * (st + 1) + 8 * half);
-                }
-                sn0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1], qf[st], sn0, 0, 0, 0);
-                sn1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[st & 1], qf[st], sn1, 0, 0, 0);
-#pragma unroll
-                for (int e = 0; e < EPS; ++e) {
-                    const int r = st * EPS + e;
-                    s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
-                    s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            qk(buf ^ 1, sn0, sn1);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
-                s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
-            }
+        for (int r = 0; r < 16; ++r) {
+            s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_new));
+            s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_new));
         }
         rescale(acc, alpha);
-
-        // phase 2: O^T += V^T P^T for chunk k, interleaved with the row sum
+        pv(buf, s0, s1);
         float sum = 0.f;
-        if constexpr (C::kBf16) {
-            const uint16_t *Vt = reinterpret_cast<const uint16_t *>(lds + buf * C::BUF + C::KBUF);
-            bf16x8 pb[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[0][e] = (__bf16)s0[e];
-                pb[1][e] = (__bf16)s0[8 + e];
-                pb[2][e] = (__bf16)s1[e];
-                pb[3][e] = (__bf16)s1[8 + e];
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                for (int cb = 0; cb < NACC; ++cb) {
-                    const uint16_t *src = Vt + (32 * cb + li) * C::VSTR + 16 * s + 8 * half;
-                    u32x2 lo = *reinterpret_cast<const u32x2 *>(src);
-                    u32x2 hi = *reinterpret_cast<const u32x2 *>(src + 4);
-                    bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], acc[cb], 0, 0, 0);
-                }
-                // 8 of the 32 probabilities of this lane per step
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sum += s0[4 * s + e] + s1[4 * s + e];
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        } else {
-            pv(buf, s0, s1);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sum += s0[r] + s1[r];
-        }
+        for (int r = 0; r < 16; ++r) sum += s0[r] + s1[r];
         const float delta = pair_sum(sum);
         l = l * alpha + delta;
         const bool wave_cont = is_p2 && __ballot(!(delta < a.tau * l)) != 0;
@@ -516,23 +339,14 @@ __global__ __launch_bounds__(64 * NW, (sizeof(T) == 2 ? 2 : 1)) void attn_kernel
 
     // epilogue: O = acc / l; lane holds O[my_row][32cb + 8q + 4half + 0..3]
     const float inv = 1.0f / l;
-    T *Op = reinterpret_cast<T *>(a.o) + ((int64_t)(b * g.Hq + h) * g.N + my_row) * D;
+    float *Op = reinterpret_cast<float *>(a.o) + ((int64_t)(b * g.Hq + h) * g.N + my_row) * D;
 #pragma unroll
     for (int cb = 0; cb < NACC; ++cb) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            T *dst = Op + 32 * cb + 8 * q + 4 * half;
-            if constexpr (C::kBf16) {
-                uint32_t o[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    o[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[cb][4 * q + e] * inv));
-                *reinterpret_cast<u32x2 *>(dst) = u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
-            } else {
-                float4 o4 = make_float4(acc[cb][4 * q] * inv, acc[cb][4 * q + 1] * inv,
-                                        acc[cb][4 * q + 2] * inv, acc[cb][4 * q + 3] * inv);
-                *reinterpret_cast<float4 *>(dst) = o4;
-            }
+            float4 o4 = make_float4(acc[cb][4 * q] * inv, acc[cb][4 * q + 1] * inv,
+                                    acc[cb][4 * q + 2] * inv, acc[cb][4 * q + 3] * inv);
+            *reinterpret_cast<float4 *>(Op + 32 * cb + 8 * q + 4 * half) = o4;
         }
     }
     if (a.exec && tid == 0) a.exec[((int64_t)b * g.Hq + h) * g.T + t] = n1 + executed2;
@@ -584,6 +398,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     unsigned char *lds = smem_raw;
     __shared__ int flags[2][NW];
     __shared__ int row_max[NW];
+    __shared__ int acc_bad[NW];
 
     const Geometry &g = a.g;
     Work wk;
@@ -748,9 +563,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     // chunk 0 only and the reference m is fixed kFastHeadroom above it, so a
     // chunk costs no max, no rescale test and no rescale; every chunk's mass
     // is checked against 2^64 instead (at most kFastHeadroom + 58 log2 units
-    // above chunk 0's max; inf and NaN fail the check too), which keeps acc and
-    // l far from overflow.  A failed check restarts the tile with the lazy
-    // running max (track = true).  acc / l and delta / l do not depend on m, so
+    // above chunk 0's max; inf and NaN fail the check too), which keeps l far
+    // from overflow, and the accumulators are checked for finiteness at the
+    // end.  A failed check restarts the tile with the lazy running max
+    // (track = true).  acc / l and delta / l do not depend on m, so
     // both attempts compute the same quantities.
     int executed2 = 0;
     // one attempt over the tile; returns true when it overflowed
@@ -867,6 +683,21 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         if (!iteration(std::integral_constant<int, 0>{}, k, sa0, sa1, sb0, sb1)) break;
         if (!iteration(std::integral_constant<int, 1>{}, k + 1, sb0, sb1, sa0, sa1)) break;
     }
+    if (!track && !overflow) {
+        // The mass check bounds every probability by 2^64, but p * V can still
+        // overflow acc when |V| is large; an accumulator that is not finite
+        // restarts the tile with the running max (probabilities <= 2^kMaxSlack).
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < NACC; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bad |= !(fabsf(acc[i][r]) < INFINITY);
+        const bool wave_bad = __ballot(bad) != 0;
+        if (lane == 0) acc_bad[wave] = wave_bad ? 1 : 0;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) overflow |= acc_bad[w] != 0;
+    }
     return overflow;
     };
     if (attempt(std::false_type{})) attempt(std::true_type{});
@@ -886,50 +717,48 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
     if (a.exec && tid == 0) a.exec[((int64_t)b * g.Hq + h) * g.T + t] = n1 + executed2;
 }
 
+// Raises a kernel's dynamic LDS limit once per process (the first launch of
+// each instantiation); later launches read the stored result.
+template <typename Kernel>
+hipError_t lds_limit_once(Kernel kernel, size_t bytes) {
+    static std::once_flag once;
+    static hipError_t result = hipSuccess;
+    std::call_once(once, [&] {
+        result = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    });
+    return result;
+}
+
+// Grid: B*Hkv*T units rounded up to a multiple of 8 (one per XCD), times G heads.
+inline unsigned attention_grid(const Geometry &g) {
+    const int64_t units = (int64_t)g.B * g.Hkv * g.T;
+    return (unsigned)(((units + 7) / 8) * 8 * g.G);
+}
+
 template <int D, int NW, bool S2O>
 hipError_t launch_bf16(const AttnParams &p, hipStream_t stream) {
     using C = BCfg<D, NW, S2O>;
-    const Geometry &g = p.g;
-    static bool attr_set = false;  // benign race: setting the same value twice is harmless
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel_bf16<D, NW, S2O>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    int64_t units = (int64_t)g.B * g.Hkv * g.T;
-    int64_t blocks = ((units + 7) / 8) * 8 * g.G;
-    hipLaunchKernelGGL((attn_kernel_bf16<D, NW, S2O>), dim3((unsigned)blocks), dim3(C::NT), C::LDS_BYTES,
+    hipError_t e = lds_limit_once(&attn_kernel_bf16<D, NW, S2O>, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_kernel_bf16<D, NW, S2O>), dim3(attention_grid(p.g)), dim3(C::NT), C::LDS_BYTES,
                        stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, int NW, bool S2O>
-hipError_t launch_one(const AttnParams &p, hipStream_t stream) {
-    using C = Cfg<T, D, NW, S2O>;
-    const Geometry &g = p.g;
-    static bool attr_set = false;  // benign race: setting the same value twice is harmless
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_kernel_staged<T, D, NW, S2O>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    int64_t units = (int64_t)g.B * g.Hkv * g.T;
-    int64_t blocks = ((units + 7) / 8) * 8 * g.G;
-    hipLaunchKernelGGL((attn_kernel_staged<T, D, NW, S2O>), dim3((unsigned)blocks), dim3(C::NT),
-                       C::LDS_BYTES, stream, p);
+template <int D, int NW, bool S2O>
+hipError_t launch_f32(const AttnParams &p, hipStream_t stream) {
+    using C = FCfg<D, NW>;
+    hipError_t e = lds_limit_once(&attn_kernel_f32<D, NW, S2O>, C::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_kernel_f32<D, NW, S2O>), dim3(attention_grid(p.g)), dim3(C::NT), C::LDS_BYTES,
+                       stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, bool S2O>
-hipError_t launch_bm(const AttnParams &p, hipStream_t s) {
-    return p.g.BM == 128 ? launch_one<T, D, 4, S2O>(p, s) : launch_one<T, D, 2, S2O>(p, s);
-}
-
-template <typename T, bool S2O>
-hipError_t launch_d(const AttnParams &p, hipStream_t s) {
-    return p.g.d == 128 ? launch_bm<T, 128, S2O>(p, s) : launch_bm<T, 64, S2O>(p, s);
+template <int D, int NW>
+hipError_t launch_f32_schedule(const AttnParams &p, bool s2o, hipStream_t s) {
+    return s2o ? launch_f32<D, NW, true>(p, s) : launch_f32<D, NW, false>(p, s);
 }
 
 }  // namespace
@@ -955,7 +784,9 @@ hipError_t launch_attention(const Geometry &g, const void *Q, const void *K, con
         return g.BM == 128 ? (s2o ? launch_bf16<64, 4, true>(p, stream) : launch_bf16<64, 4, false>(p, stream))
                            : (s2o ? launch_bf16<64, 2, true>(p, stream) : launch_bf16<64, 2, false>(p, stream));
     }
-    return s2o ? launch_d<float, true>(p, stream) : launch_d<float, false>(p, stream);
+    if (g.d == 128)
+        return g.BM == 128 ? launch_f32_schedule<128, 4>(p, s2o, stream) : launch_f32_schedule<128, 2>(p, s2o, stream);
+    return g.BM == 128 ? launch_f32_schedule<64, 4>(p, s2o, stream) : launch_f32_schedule<64, 2>(p, s2o, stream);
 }
 
 }  // namespace s2o

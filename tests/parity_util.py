@@ -103,11 +103,14 @@ def sample_tiles(w, heads, n_random, seed, seg_len=None):
     return sorted(tiles)
 
 
-def compare(run: GpuRun, tiles, tau, o_gpu, ex_gpu, check_lists=True):
-    """Compare the given tiles against the oracle; returns a report dict."""
+def compare(run: GpuRun, tiles, tau, o_gpu, ex_gpu, check_lists=True, res=None):
+    """Compare the given tiles against the oracle; returns a report dict.
+    res: the oracle's result for these tiles (attn_tiles with want_lists=True),
+    computed here when not given."""
     w, po = run.w, run.po
     BM = w.tile_m
-    res = oracle.attn_tiles(po, run.x["q"], run.x["k"], run.x["v"], tiles, tau, want_lists=True)
+    if res is None:
+        res = oracle.attn_tiles(po, run.x["q"], run.x["k"], run.x["v"], tiles, tau, want_lists=True)
     ex = ex_gpu.cpu().numpy()
     rep = dict(tiles=len(tiles), near_tau=0, list_mismatch=0, exec_mismatch=0, max_abs=0.0,
                sum_abs=0.0, n=0)

@@ -130,7 +130,8 @@ def test_workspace_sizes():
     ("batch", 0, INVALID), ("heads_q", 3, INVALID), ("seq_len", 1000, INVALID),
     ("seg_len", 200, INVALID), ("head_dim", 96, UNSUPPORTED), ("tile_m", 256, UNSUPPORTED),
     ("tile_n", 32, UNSUPPORTED), ("dtype", 7, INVALID), ("causal", 2, INVALID),
-    ("scale", float("nan"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 16, INVALID), ("list_granularity", -1, INVALID),
+    ("scale", float("nan"), INVALID), ("scale", 0.0, INVALID), ("scale", -0.125, INVALID),
+    ("scale", float("inf"), INVALID), ("tile_m", 96, INVALID), ("list_granularity", 16, INVALID), ("list_granularity", -1, INVALID),
     ("list_granularity", 4 | 8, UNSUPPORTED),  # query permutation with shared lists
     ("seq_len", 1 << 23, UNSUPPORTED)])  # one head's K at d = 128 would span 2^31 bytes
 def test_problem_validation(field, value, code):

@@ -163,6 +163,23 @@ size_t s2o_score_workspace_bytes(const s2o_problem *p);
 s2o_status s2o_score(const s2o_problem *p, const void *Q, const void *K, float *scores,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* s2o_score without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments and results as s2o_score, bit for
+ * bit; the workspace is a static device array of
+ * S2O_SCORE_NOALLOC_MAX_WORKSPACE bytes that every GPU the library runs on
+ * holds until the process ends (its address is looked up on the first call on
+ * each device).  The call allocates nothing.  Calls on one GPU share that
+ * array, so calls that overlap on one GPU (other streams, other host threads)
+ * race: serialise them.  Problems whose s2o_score_workspace_bytes exceeds the
+ * maximum return S2O_ERR_WORKSPACE before anything is enqueued (64 MiB holds
+ * every list form of one 128K-token Llama-3.1-8B-shaped layer).
+ * Errors: as s2o_score, plus WORKSPACE for a problem above the maximum and HIP
+ * when the array's device address cannot be obtained. */
+#define S2O_SCORE_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+s2o_status s2o_score_noalloc(const s2o_problem *p, const void *Q, const void *K, float *scores,
+                             void *stream);
+
 /* Bytes of device workspace s2o_build_index needs.  0 if the problem is invalid. */
 size_t s2o_build_index_workspace_bytes(const s2o_problem *p);
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libs2o.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["abi.cpp", "attn_fwd.hip", "score.hip", "sort.hip"]
+SOURCES = ["abi.cpp", "attn_fwd.hip", "score.hip", "sort.hip", "noalloc.hip"]
 ARCH = os.environ.get("S2O_OFFLOAD_ARCH", "gfx950")
 
 

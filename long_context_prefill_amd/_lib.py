@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libs2o.so")
 
 # every symbol include/s2o.h declares
 EXPORTS = ("s2o_check_problem", "s2o_list_entries", "s2o_list_offset",
-           "s2o_score_workspace_bytes", "s2o_score", "s2o_build_index_workspace_bytes",
+           "s2o_score_workspace_bytes", "s2o_score", "s2o_score_noalloc", "s2o_build_index_workspace_bytes",
            "s2o_build_index", "s2o_attn_fwd", "dense_attn_fwd", "s2o_status_string")
 
 STATUS = {0: "S2O_OK", -1: "S2O_ERR_INVALID_ARG", -2: "S2O_ERR_UNSUPPORTED",
@@ -65,6 +65,7 @@ def lib():
             "s2o_list_offset": (i64, [P, i32, i32, i32]),
             "s2o_score_workspace_bytes": (sz, [P]),
             "s2o_score": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+            "s2o_score_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp]),
             "s2o_build_index_workspace_bytes": (sz, [P]),
             "s2o_build_index": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
             "s2o_attn_fwd": (ctypes.c_int, [P, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]),
@@ -174,6 +175,22 @@ def s2o_score(p: Problem, q: torch.Tensor, k: torch.Tensor, scores: Optional[tor
                          _dev(scores, "scores", torch.float32), _dev(workspace, "workspace"),
                          workspace.numel(), _stream())
     _raise("s2o_score", st)
+    return scores
+
+
+# bytes of the static workspace s2o_score_noalloc uses (S2O_SCORE_NOALLOC_MAX_WORKSPACE)
+SCORE_NOALLOC_MAX_WORKSPACE = 64 << 20
+
+
+def s2o_score_noalloc(p: Problem, q: torch.Tensor, k: torch.Tensor,
+                      scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """s2o_score with the library's static workspace (no caller workspace)."""
+    dt = _tdtype(p)
+    if scores is None:
+        scores = torch.empty(list_entries(p), dtype=torch.float32, device=q.device)
+    st = lib().s2o_score_noalloc(ctypes.byref(p), _dev(q, "q", dt), _dev(k, "k", dt),
+                                 _dev(scores, "scores", torch.float32), _stream())
+    _raise("s2o_score_noalloc", st)
     return scores
 
 

@@ -217,3 +217,27 @@ def test_query_permutation_layout_and_validation(lists):
     # fp32 inputs and segments beyond the in-LDS query sort are not compiled
     assert s2o.check_problem(base_problem(dtype=0, qperm=True)) == UNSUPPORTED
     assert s2o.check_problem(base_problem(seq_len=32768, seg_len=16384, qperm=True)) == UNSUPPORTED
+
+
+def test_score_noalloc_rejects_problems_above_its_static_workspace():
+    """s2o_score_noalloc validates the problem and its workspace size on the host
+    and returns before touching the GPU: an invalid problem is INVALID_ARG, one
+    whose score workspace exceeds the static array is WORKSPACE, and the header's
+    limit is the one the binding states."""
+    text = open(HEADER).read()
+    m = re.search(r"#define S2O_SCORE_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == s2o.SCORE_NOALLOC_MAX_WORKSPACE
+    L = s2o.lib()
+    fake, nul = ctypes.c_void_p(1 << 20), ctypes.c_void_p(0)
+    big = base_problem(batch=8, heads_q=32, heads_kv=8, seq_len=131072, seg_len=8192)
+    assert s2o.score_workspace_bytes(big) > s2o.SCORE_NOALLOC_MAX_WORKSPACE
+    assert L.s2o_score_noalloc(ctypes.byref(big), fake, fake, fake, nul) == WORKSPACE
+    bad = base_problem(seq_len=1000)
+    assert L.s2o_score_noalloc(ctypes.byref(bad), fake, fake, fake, nul) == INVALID
+    head = base_problem(batch=1, heads_q=32, heads_kv=8, seq_len=131072, seg_len=8192)
+    for lists in ("tile", "segment", "tile_blocks"):
+        for qperm in (False, True):
+            p = base_problem(batch=1, heads_q=32, heads_kv=8, seq_len=131072, seg_len=8192, lists=lists,
+                             qperm=qperm)
+            assert s2o.score_workspace_bytes(p) <= s2o.SCORE_NOALLOC_MAX_WORKSPACE, (lists, qperm)
+    assert s2o.score_workspace_bytes(head) > 0

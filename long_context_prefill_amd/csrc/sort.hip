@@ -12,16 +12,20 @@
 // straddle two lists.  Two data passes instead of four LSD passes:
 //
 //   1. bucket pass (one stable MSD step).  Each list's scores are split into
-//      256 buckets of equal width between the list's minimum and maximum,
-//      highest values first.  The bucket function is monotone in the score,
-//      so every bucket holds a contiguous range of the final order, and equal
-//      scores share a bucket.  minmax (per block) -> hist (per block, LDS
-//      atomics) -> scan (per list) -> scatter (per block: stable rank by a
-//      wave-level multisplit, staged in LDS, written as contiguous bucket
-//      runs of (key, position) pairs).  Within a bucket, positions ascend;
-//      the steps below do not rely on it (the multisplit is kept because LDS
-//      atomics on the few crowded buckets of a peaked score distribution
-//      serialize and cost more than it).
+//      256 buckets of equal width between the minimum and maximum of a sample
+//      of the list (every 16th run of 64 scores), highest values first; scores
+//      outside the sampled range join the end buckets.  The bucket function is
+//      monotone in the score (clamping keeps it so), so every bucket holds a
+//      contiguous range of the final order, and equal scores share a bucket;
+//      the sample only affects how evenly the buckets fill.  plan (per list:
+//      sample bounds) -> hist (per block, LDS atomics) -> scan (per list) ->
+//      scatter (per block: stable rank by a wave-level multisplit, staged in
+//      LDS, written as contiguous bucket runs of (key, position) pairs; each
+//      XCD takes a contiguous share of the blocks, so the partial cache lines
+//      where neighbouring blocks' runs meet are merged in one L2).  Within a
+//      bucket, positions ascend; the steps below do not rely on it (the
+//      multisplit is kept because LDS atomics on the few crowded buckets of a
+//      peaked score distribution serialize and cost more than it).
 //   2. range sort.  Each workgroup owns the buckets that start inside its
 //      chunk of C output positions, i.e. a contiguous range of the list, and
 //      orders it without radix passes: NSB sub-buckets of equal score width
@@ -121,75 +125,41 @@ __device__ inline ListRef list_ref(const Geometry &g, int lid) {
 }
 
 // Bucket function of pass 1: NB buckets of equal width over [lo, hi], the
-// highest scores in digit 0.  Non-increasing in x, so buckets never interleave.
+// highest scores in digit 0, values outside [lo, hi] clamped to the end
+// buckets.  Non-increasing in x, so buckets never interleave.
 struct Buckets {
     float lo, sc;  // sc = 0: a single bucket
 };
 __device__ inline uint32_t bucket_digit(float x, Buckets r) {
     if (!(r.sc > 0.f)) return NB - 1;
-    const float f = (x - r.lo) * r.sc;  // in [0, NB(1+eps)] since lo <= x <= hi
-    int b = (int)f;
-    b = b < NB - 1 ? b : NB - 1;
-    return (uint32_t)(NB - 1 - b);
+    const float f = fminf(fmaxf((x - r.lo) * r.sc, 0.f), (float)(NB - 1));
+    return (uint32_t)(NB - 1 - (int)f);
 }
 
-// Bucket parameters of the list owning block `blk` (every thread gets them).
-// The reduction order is fixed, so hist and scatter agree bit for bit.
-__device__ Buckets list_buckets(const Geometry &g, const int32_t *blk_list, const float *blk_mm,
-                                int E, float *sh) {
-    const ListRef L = list_ref(g, blk_list[blockIdx.x]);
-    const int64_t b0 = L.off / E, nb = L.len / E;
-    if (threadIdx.x < 64) {
-        float lo = INFINITY, hi = -INFINITY;
-        for (int64_t i = threadIdx.x; i < nb; i += 64) {
-            lo = fminf(lo, blk_mm[2 * (b0 + i)]);
-            hi = fmaxf(hi, blk_mm[2 * (b0 + i) + 1]);
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            lo = fminf(lo, __shfl_xor(lo, o));
-            hi = fmaxf(hi, __shfl_xor(hi, o));
-        }
-        if (threadIdx.x == 0) {
-            sh[0] = lo;
-            sh[1] = hi;
-        }
-    }
-    __syncthreads();
-    const float lo = sh[0], d = sh[1] - lo;
-    float sc = d > 0.f ? (float)NB / d : 0.f;
-    if (!(sc < INFINITY)) sc = 0.f;  // d overflowed or is denormal-small
-    return {lo, sc};
-}
+// Scores a list's bounds are sampled from: every SAMPLE_STRIDE-th run of
+// SAMPLE_RUN consecutive scores (a run is 256 bytes).
+constexpr int SAMPLE_RUN = 64;
+constexpr int SAMPLE_STRIDE = 16;
 
-// One workgroup per list: records which list every block belongs to, and
-// empties the overflow queue.
-__global__ __launch_bounds__(THREADS) void plan_kernel(int32_t *__restrict__ blk_list,
+// One workgroup per list: records which list every block belongs to, the
+// list's bucket parameters from the sampled minimum and maximum, and empties
+// the overflow queues.
+__global__ __launch_bounds__(THREADS) void plan_kernel(const float *__restrict__ scores,
+                                                       int32_t *__restrict__ blk_list, Buckets *__restrict__ list_bk,
                                                        int32_t *__restrict__ queue_len, Geometry g, int E) {
+    __shared__ float red[2][NWAVES];
     if (blockIdx.x == 0 && threadIdx.x < 2) queue_len[threadIdx.x] = 0;  // both queues
     const ListRef L = list_ref(g, blockIdx.x);
     const int64_t b0 = L.off / E, nb = L.len / E;
     for (int64_t i = threadIdx.x; i < nb; i += THREADS) blk_list[b0 + i] = (int32_t)blockIdx.x;
-}
-
-// Per block: minimum and maximum score.
-__global__ __launch_bounds__(THREADS) void minmax_kernel(const float *__restrict__ scores,
-                                                         float *__restrict__ blk_mm, int E) {
-    __shared__ float red[2][NWAVES];
-    const float *s = scores + (int64_t)blockIdx.x * E;
+    if (L.len == 0) return;
+    // every length is a multiple of SAMPLE_RUN; sampled runs 0, STRIDE, 2*STRIDE, ...
+    const int64_t runs = (L.len / SAMPLE_RUN + SAMPLE_STRIDE - 1) / SAMPLE_STRIDE;
+    constexpr int PIECES = SAMPLE_RUN / 4;  // float4 pieces per run
     float lo = INFINITY, hi = -INFINITY;
-    // every load of the thread is issued before the first is used
-    constexpr int PER = MAX_BLOCK / (4 * THREADS);
-    float4 xs[PER];
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-        const int i = 4 * threadIdx.x + it * 4 * THREADS;
-        if (i < E) xs[it] = *reinterpret_cast<const float4 *>(s + i);
-    }
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-        if (4 * threadIdx.x + it * 4 * THREADS >= E) break;
-        const float4 x = xs[it];
+    for (int64_t i = threadIdx.x; i < runs * PIECES; i += THREADS) {
+        const int64_t pos = (i / PIECES) * SAMPLE_STRIDE * SAMPLE_RUN + (i % PIECES) * 4;
+        const float4 x = *reinterpret_cast<const float4 *>(scores + L.off + pos);
         lo = fminf(fminf(lo, x.x), fminf(x.y, fminf(x.z, x.w)));
         hi = fmaxf(fmaxf(hi, x.x), fmaxf(x.y, fmaxf(x.z, x.w)));
     }
@@ -209,20 +179,22 @@ __global__ __launch_bounds__(THREADS) void minmax_kernel(const float *__restrict
             lo = fminf(lo, red[0][w]);
             hi = fmaxf(hi, red[1][w]);
         }
-        blk_mm[2 * blockIdx.x] = lo;
-        blk_mm[2 * blockIdx.x + 1] = hi;
+        const float d = hi - lo;
+        float sc = d > 0.f ? (float)NB / d : 0.f;
+        if (!(sc < INFINITY)) sc = 0.f;  // d overflowed or is denormal-small
+        list_bk[blockIdx.x] = {lo, sc};
     }
 }
 
 // Per block: bucket histogram (order-free, so LDS atomics).
 __global__ __launch_bounds__(THREADS) void hist_kernel(const float *__restrict__ scores,
                                                        const int32_t *__restrict__ blk_list,
-                                                       const float *__restrict__ blk_mm,
-                                                       int32_t *__restrict__ hist, Geometry g, int E) {
+                                                       const Buckets *__restrict__ list_bk,
+                                                       int32_t *__restrict__ hist, int E) {
     __shared__ int cnt[NWAVES][NB];
-    __shared__ float sh[2];
     for (int i = threadIdx.x; i < NWAVES * NB; i += THREADS) (&cnt[0][0])[i] = 0;
-    const Buckets bk = list_buckets(g, blk_list, blk_mm, E, sh);  // synchronises
+    const Buckets bk = list_bk[blk_list[blockIdx.x]];
+    __syncthreads();
     const int wave = threadIdx.x >> 6;
     const float *s = scores + (int64_t)blockIdx.x * E;
     constexpr int PER = MAX_BLOCK / (4 * THREADS);
@@ -296,9 +268,9 @@ __global__ __launch_bounds__(NB) void scan_kernel(int32_t *__restrict__ hist, in
 template <int E>
 __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restrict__ scores,
                                                           const int32_t *__restrict__ blk_list,
-                                                          const float *__restrict__ blk_mm,
+                                                          const Buckets *__restrict__ list_bk,
                                                           const int32_t *__restrict__ hist,
-                                                          u32x2 *__restrict__ pairs, Geometry g) {
+                                                          u32x2 *__restrict__ pairs, Geometry g, int64_t nblocks) {
     constexpr int NWV = E >= 256 ? NWAVES : E / 64;  // waves holding entries
     constexpr int ROUNDS = E / (64 * NWV);           // wave w owns [w*E/NWV, (w+1)*E/NWV)
     __shared__ int cnt[NWAVES][NB];  // per-wave digit counters, then staging offsets
@@ -306,13 +278,19 @@ __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restric
     __shared__ int dglob[NB];        // run start of each digit relative to the block, minus dstart
     __shared__ u32x2 stage[E];       // (key, position) sorted by digit
     __shared__ uint8_t sdig[E];
-    __shared__ float sh[2];
+    // XCD-aware order: block ids are dispatched round-robin over the 8 XCDs;
+    // XCD x takes the contiguous blocks [x*per, (x+1)*per), so the blocks of a
+    // list, whose bucket runs abut, write through the same L2
+    const int64_t per = gridDim.x / 8;
+    const int64_t blk = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+    if (blk >= nblocks) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     for (int i = tid; i < NWAVES * NB; i += THREADS) (&cnt[0][0])[i] = 0;
-    for (int v = tid; v < NB; v += THREADS) dglob[v] = hist[(int64_t)blockIdx.x * NB + v];
-    const Buckets bk = list_buckets(g, blk_list, blk_mm, E, sh);  // synchronises
-    const int64_t base = (int64_t)blockIdx.x * E;
-    const int32_t pos0 = (int32_t)(base - list_ref(g, blk_list[blockIdx.x]).off);
+    for (int v = tid; v < NB; v += THREADS) dglob[v] = hist[blk * NB + v];
+    const Buckets bk = list_bk[blk_list[blk]];
+    __syncthreads();
+    const int64_t base = blk * E;
+    const int32_t pos0 = (int32_t)(base - list_ref(g, blk_list[blk]).off);
 
     float x[ROUNDS];
     uint32_t dig[ROUNDS];
@@ -554,12 +532,13 @@ __device__ inline float key_score(uint32_t key) {
 // (clustered or repeated scores); the caller then sorts the range otherwise.
 template <int R>
 __device__ __forceinline__ bool rank_in_sub_buckets(const u32x2 *__restrict__ in, int32_t *__restrict__ out,
-                                                    int m, u32x2 *stage, int *sbc, int *red) {
+                                                    int m, uint64_t *stage, int *sbc, int *red) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wbase = wave * R * 64 + lane;
+    // Entries as (key << 32 | position): one 64-bit comparison orders them.
     // Padding entries (index >= m) take the same steps without branches: they
     // count into sbc[NSB], land in the stage's tail [m, R*THREADS) and write nothing.
-    u32x2 e[R];
+    uint64_t e[R];
     int dig[R], slot[R];
     uint32_t kmin = 0xFFFFFFFFu, nkmax = 0xFFFFFFFFu;  // nkmax = ~(largest key)
 #pragma unroll
@@ -567,9 +546,9 @@ __device__ __forceinline__ bool rank_in_sub_buckets(const u32x2 *__restrict__ in
         const int i = wbase + 64 * r;
         const bool real = i < m;
         const u32x2 v = in[real ? i : m - 1];  // in bounds for every lane, no branch
-        e[r].x = real ? v.x : 0xFFFFFFFFu;
-        e[r].y = real ? v.y : 0u;
-        kmin = min(kmin, e[r].x);
+        const uint32_t key = real ? v.x : 0xFFFFFFFFu;
+        e[r] = ((uint64_t)key << 32) | (real ? v.y : 0u);
+        kmin = min(kmin, key);
         nkmax = min(nkmax, real ? ~v.x : 0xFFFFFFFFu);
     }
     for (int i = tid; i <= NSB; i += THREADS) sbc[i] = 0;
@@ -595,7 +574,7 @@ __device__ __forceinline__ bool rank_in_sub_buckets(const u32x2 *__restrict__ in
     const bool spread = width > 0.f && width < INFINITY && scale < INFINITY;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int d = spread ? min((int)((top - key_score(e[r].x)) * scale), NSB - 1) : 0;
+        const int d = spread ? min((int)((top - key_score((uint32_t)(e[r] >> 32))) * scale), NSB - 1) : 0;
         dig[r] = wbase + 64 * r < m ? d : NSB;
         slot[r] = atomicAdd(&sbc[dig[r]], 1);
     }
@@ -647,12 +626,9 @@ __device__ __forceinline__ bool rank_in_sub_buckets(const u32x2 *__restrict__ in
         const int b0 = sbc[d], b1 = d < NSB ? sbc[d + 1] : b0;
         int rank = b0;
         if (b1 - b0 > 1) {
-            for (int j = b0; j < b1; ++j) {
-                const u32x2 o = stage[j];
-                rank += (o.x < e[r].x || (o.x == e[r].x && o.y < e[r].y)) ? 1 : 0;
-            }
+            for (int j = b0; j < b1; ++j) rank += stage[j] < e[r] ? 1 : 0;
         }
-        if (d < NSB) out[rank] = (int32_t)e[r].y;
+        if (d < NSB) out[rank] = (int32_t)(uint32_t)e[r];
     }
     return true;
 }
@@ -674,7 +650,7 @@ __global__ __launch_bounds__(THREADS, 4) void range_sort_kernel(const u32x2 *__r
                                                                 Overflow *__restrict__ queue,
                                                                 int32_t *__restrict__ queue_len,
                                                                 Geometry g, int E) {
-    __shared__ u32x2 stage[RANGE_CAP];
+    __shared__ uint64_t stage[RANGE_CAP];
     __shared__ int sbc[NSB + 1];
     __shared__ int sred[4 * NWAVES];
     const int tid = threadIdx.x;
@@ -749,7 +725,7 @@ __global__ __launch_bounds__(THREADS, 4) void queued_range_kernel(const u32x2 *_
                                                                   Overflow *__restrict__ queue2,
                                                                   int32_t *__restrict__ queue2_len,
                                                                   Geometry g) {
-    __shared__ u32x2 stage[CAP];
+    __shared__ uint64_t stage[CAP];
     __shared__ int sbc[NSB + 1];
     __shared__ int sred[4 * NWAVES];
     const int tid = threadIdx.x;
@@ -904,7 +880,7 @@ int range_chunk(const Geometry &g) {
 struct SortWs {
     u32x2 *pairs, *scratch;
     int32_t *hist, *blk_list, *bstart, *queue_len;
-    float *blk_mm;
+    Buckets *list_bk;
     Overflow *queue, *queue2;
     size_t bytes;
 };
@@ -926,8 +902,8 @@ SortWs carve(const Geometry &g, void *base) {
     off += align256((size_t)nblocks * NB * 4);
     w.blk_list = reinterpret_cast<int32_t *>(p + off);
     off += align256((size_t)nblocks * 4);
-    w.blk_mm = reinterpret_cast<float *>(p + off);
-    off += align256((size_t)nblocks * 8);
+    w.list_bk = reinterpret_cast<Buckets *>(p + off);
+    off += align256((size_t)lists * sizeof(Buckets));
     w.bstart = reinterpret_cast<int32_t *>(p + off);
     off += align256((size_t)lists * (NB + 1) * 4);
     w.queue = reinterpret_cast<Overflow *>(p + off);  // at most one entry per chunk
@@ -946,13 +922,13 @@ hipError_t run_sort(const Geometry &g, const float *scores, int32_t *idx, const 
     constexpr int C = E < MAX_CHUNK ? E : MAX_CHUNK;  // = range_chunk(g)
     const int64_t nblocks = g.list_entries / E;
     const unsigned lists = (unsigned)((int64_t)g.B * g.Hq * lists_per_head(g));
-    hipLaunchKernelGGL(plan_kernel, dim3(lists), dim3(THREADS), 0, stream, w.blk_list, w.queue_len, g, E);
-    hipLaunchKernelGGL(minmax_kernel, dim3((unsigned)nblocks), dim3(THREADS), 0, stream, scores, w.blk_mm, E);
+    hipLaunchKernelGGL(plan_kernel, dim3(lists), dim3(THREADS), 0, stream, scores, w.blk_list, w.list_bk,
+                       w.queue_len, g, E);
     hipLaunchKernelGGL(hist_kernel, dim3((unsigned)nblocks), dim3(THREADS), 0, stream, scores, w.blk_list,
-                       w.blk_mm, w.hist, g, E);
+                       w.list_bk, w.hist, E);
     hipLaunchKernelGGL(scan_kernel, dim3(lists), dim3(NB), 0, stream, w.hist, w.bstart, g, E);
-    hipLaunchKernelGGL(scatter_kernel<E>, dim3((unsigned)nblocks), dim3(THREADS), 0, stream, scores,
-                       w.blk_list, w.blk_mm, w.hist, w.pairs, g);
+    hipLaunchKernelGGL(scatter_kernel<E>, dim3((unsigned)(((nblocks + 7) / 8) * 8)), dim3(THREADS), 0, stream, scores,
+                       w.blk_list, w.list_bk, w.hist, w.pairs, g, nblocks);
     hipLaunchKernelGGL(range_sort_kernel<C>, dim3((unsigned)(g.list_entries / C)), dim3(THREADS), 0, stream,
                        w.pairs, idx, w.blk_list, w.bstart, w.queue, w.queue_len, g, E);
     hipLaunchKernelGGL(queued_range_kernel, dim3(QUEUED_GRID), dim3(THREADS), 0, stream, w.pairs, idx, w.queue,

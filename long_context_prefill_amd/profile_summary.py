@@ -134,6 +134,57 @@ def kernel_counter_table(paths, kernels):
     return out
 
 
+def l2_report(a, copy, avg):
+    """Per kernel: L2 hit rate TCC_HIT / (TCC_HIT + TCC_MISS), and the bytes of
+    requests L2 sends towards DRAM addresses: TCC_EA0_RDREQ_DRAM_32B counts
+    32-byte read sectors and TCC_EA0_WRREQ_DRAM 64-byte write requests (for the
+    plain copy kernel of a.copy_bytes both come to exactly that many bytes; the
+    scale below checks it).  Counters are averaged over a kernel's dispatches,
+    except the copy's, whose largest dispatch is the calibration copy.  Prints a
+    table and returns {kernel: {...}}."""
+    def counters(path):
+        per = collections.defaultdict(lambda: collections.defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        return per
+
+    def mean(v):
+        return sum(v) / len(v)
+
+    def copy_value(per, counter):
+        return max(max(per[k][counter]) for k in per if "copyBuffer" in k)
+
+    out = collections.defaultdict(dict)
+    if a.hitmiss:
+        for k, c in counters(a.hitmiss).items():
+            hit, miss = mean(c.get("TCC_HIT_sum", [0.0])), mean(c.get("TCC_MISS_sum", [0.0]))
+            if hit + miss > 0:
+                out[short(k)]["l2_hit_rate"] = hit / (hit + miss)
+    for path, counter, unit, key, what in ((a.dram_read, "TCC_EA0_RDREQ_DRAM_32B_sum", 32.0, "dram_read_bytes", "reads"),
+                                           (a.dram_write, "TCC_EA0_WRREQ_DRAM_sum", 64.0, "dram_write_bytes", "writes")):
+        if not path:
+            continue
+        per = counters(path)
+        scale = a.copy_bytes / (unit * copy_value(per, counter))
+        print(f"calibration: plain copy {what} {unit * copy_value(per, counter) / 1e9:.4f} GB of DRAM-destined "
+              f"requests ({counter} x {unit:.0f} B) -> scale x{scale:.3f}")
+        for k, c in per.items():
+            if counter in c:
+                out[short(k)][key] = unit * (max(c[counter]) if "copyBuffer" in k else mean(c[counter])) * scale
+    print(f"\n{'kernel':44s} {'L2 hit':>7s} {'DRAM rd GB':>11s} {'DRAM wr GB':>11s} {'GB/s':>8s}")
+    for n, r in out.items():
+        if n.startswith("at::") or "void at" in n:
+            continue
+        ms = avg.get(n)
+        rd, wr = r.get("dram_read_bytes"), r.get("dram_write_bytes")
+        bw = (rd + wr) / (ms * 1e-3) / 1e9 if (ms and rd is not None and wr is not None) else float("nan")
+        hit = r.get("l2_hit_rate")
+        print(f"{n:44s} {100 * hit if hit is not None else float('nan'):6.1f}% "
+              f"{rd / 1e9 if rd is not None else float('nan'):11.2f} "
+              f"{wr / 1e9 if wr is not None else float('nan'):11.2f} {bw:8.0f}")
+    return out
+
+
 def main_kernel_counters(a):
     print(f"command: {a.command}\n")
     for n, d in kernel_counter_table(a.counters, a.kernels).items():
@@ -199,6 +250,9 @@ def main():
     ap.add_argument("--traffic-out", help="write the S2O attention kernel's traffic record (JSON) here")
     ap.add_argument("--workload", default="", help="workload named in the traffic record")
     ap.add_argument("--source", nargs="+", help="kernel sources whose hash the traffic record holds")
+    ap.add_argument("--hitmiss", help="counter CSV with TCC_HIT_sum and TCC_MISS_sum")
+    ap.add_argument("--dram-read", help="counter CSV with TCC_EA0_RDREQ_DRAM_sum and TCC_EA0_RDREQ_DRAM_32B_sum")
+    ap.add_argument("--dram-write", help="counter CSV with TCC_EA0_WRREQ_DRAM_sum")
     a = ap.parse_args()
     print(f"command: {a.command}\n")
     print(f"{'kernel':44s} {'calls':>5s} {'avg ms':>10s} {'total ms':>10s} {'%':>6s}")
@@ -229,6 +283,10 @@ def main():
         if n.startswith("at::") or "void at" in n:
             continue
         print(f"{n:44s} {fb / 1e9:10.2f} {wb / 1e9:10.2f} {ms if ms else float('nan'):8.3f} {bw:8.0f}")
+    l2 = l2_report(a, copy, avg) if (a.hitmiss or a.dram_read or a.dram_write) else {}
+    for n, r in l2.items():
+        if n in out:
+            out[n].update(r)
     if a.json_out:
         json.dump(out, open(a.json_out, "w"), indent=1)
     if a.traffic_out:
@@ -240,6 +298,14 @@ def main():
                        "plain copy in the same run); these count every request that leaves L2, "
                        "Infinity Cache hits included",
                "command": a.command, "kernel_source_sha256_16": sources_hash(a.source) if a.source else None}
+        if "dram_read_bytes" in k and "dram_write_bytes" in k:
+            rec["dram_bytes_per_launch"] = k["dram_read_bytes"] + k["dram_write_bytes"]
+            rec["dram_note"] = ("TCC_EA0_RDREQ_DRAM_32B x 32 B + TCC_EA0_WRREQ_DRAM x 64 B (a plain copy "
+                                "reads and writes exactly its size by them): requests that leave L2 for local "
+                                "HBM addresses, Infinity Cache hits included (no counter here separates those "
+                                "from HBM reads)")
+        if "l2_hit_rate" in k:
+            rec["l2_hit_rate"] = k["l2_hit_rate"]
         json.dump(rec, open(a.traffic_out, "w"), indent=1)
         open(a.traffic_out, "a").write("\n")
 

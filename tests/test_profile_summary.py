@@ -37,3 +37,37 @@ def test_kernel_counter_table_shares(tmp_path):
     assert abs(d["lds_busy"] - 0.25) < 1e-12
     assert abs(d["lds_bank_conflict_share"] - 0.2) < 1e-12
     assert (d["wave_issuing"], d["wave_waiting_issue"], d["wave_waiting_counters_barrier"]) == (0.4, 0.35, 0.25)
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for k, c, v in rows:
+            wr.writerow({"Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+def test_l2_report_scales_by_the_copy(tmp_path):
+    """L2 hit rate is hits over hits plus misses; DRAM-destined bytes are 32-byte
+    read sectors and 64-byte write requests, averaged over a kernel's dispatches
+    except the copy's largest, which fixes the scale (here the copy's counters
+    give exactly its size, so the scale is 1)."""
+    import types
+    attn = "void s2o::(anonymous namespace)::attn_kernel_bf16<128, 4, true>(x)"
+    copy = "__amd_rocclr_copyBuffer"
+    hm, rd, wr = tmp_path / "hm.csv", tmp_path / "rd.csv", tmp_path / "wr.csv"
+    _counter_csv(hm, [(attn, "TCC_HIT_sum", 30.0), (attn, "TCC_MISS_sum", 70.0),
+                      (attn, "TCC_HIT_sum", 50.0), (attn, "TCC_MISS_sum", 50.0)])
+    # copy of 128 KiB: 4096 sectors of 32 B read, 2048 requests of 64 B written; a small copy beside it
+    _counter_csv(rd, [(copy, "TCC_EA0_RDREQ_DRAM_32B_sum", 4096.0), (copy, "TCC_EA0_RDREQ_DRAM_32B_sum", 8.0),
+                      (attn, "TCC_EA0_RDREQ_DRAM_32B_sum", 300.0), (attn, "TCC_EA0_RDREQ_DRAM_32B_sum", 100.0)])
+    _counter_csv(wr, [(copy, "TCC_EA0_WRREQ_DRAM_sum", 2048.0), (copy, "TCC_EA0_WRREQ_DRAM_sum", 0.0),
+                      (attn, "TCC_EA0_WRREQ_DRAM_sum", 16.0)])
+    a = types.SimpleNamespace(hitmiss=str(hm), dram_read=str(rd), dram_write=str(wr), copy_bytes=128 * 1024.0)
+    out = ps.l2_report(a, copy, {"s2o_attn_fwd (S2O schedule)": 1.0})
+    r = out["s2o_attn_fwd (S2O schedule)"]
+    assert abs(r["l2_hit_rate"] - 0.4) < 1e-12
+    assert abs(r["dram_read_bytes"] - 32 * 200) < 1e-9
+    assert abs(r["dram_write_bytes"] - 16 * 64) < 1e-9
+    assert abs(out[ps.short(copy)]["dram_read_bytes"] - 128 * 1024) < 1e-9
+    assert abs(out[ps.short(copy)]["dram_write_bytes"] - 128 * 1024) < 1e-9

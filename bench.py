@@ -583,6 +583,18 @@ def measure(ctx, mode, taus, steps, warmup, refine=True, sample=(), after=None, 
 
 # ---------------------------------------------------------- the CPU leg -------
 
+def host_cpu_model(path="/proc/cpuinfo"):
+    """The host CPU's model name (first 'model name' line), or None."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return " ".join(line.split(":", 1)[1].split())[:48]
+    except OSError:
+        pass
+    return None
+
+
 def cpu_leg(ctx, sample, tau, p, idx, out, exec_tiles, dense_rows_per_tile=4):
     """The oracle on the sample (pool, score, order, pass 1, pass 2 at tau) with
     all host threads: its time, scaled to the layer by executed keys, is the CPU
@@ -636,7 +648,7 @@ def cpu_leg(ctx, sample, tau, p, idx, out, exec_tiles, dense_rows_per_tile=4):
     sample_keys = int(res["n_exec"].sum()) * w.tile_n
     layer_keys = int(exec_tiles.sum()) * w.tile_n
     cpu = {"value": round(dt * 1e3 * layer_keys / max(sample_keys, 1), 1), "unit": "ms", "cores": threads,
-           "kind": "oracle", "extrapolated": True,
+           "cpu": host_cpu_model(), "kind": "oracle", "extrapolated": True,
            "sample": (f"{len(sample)} tiles (heads 0,9,18,27: first+last of each segment; 16 seeded) at tau*, "
                       f"{dt:.1f} s, x executed keys {layer_keys}/{sample_keys}")}
     log(f"parity {parity}")

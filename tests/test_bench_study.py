@@ -221,7 +221,8 @@ def test_record_of_a_full_run_fits_the_driver(monkeypatch):
     parity = {"tiles": 144, "tau": main["tau"], "list_mismatch": 0, "exec_mismatch": 0, "near_tau": 1,
               "max_abs": 0.0123456789, "mean_abs": 0.000412345678, "ok": True, "dense_rows": 576,
               "dense_max_abs": 0.00812345678, "dense_mean_abs": 0.000312345678}
-    cpu = {"value": 1384332.123, "unit": "ms", "cores": 16, "kind": "oracle", "extrapolated": True,
+    cpu = {"value": 1384332.123, "unit": "ms", "cores": 16, "cpu": "AMD EPYC 9575F 64-Core Processor" + " " * 16,
+           "kind": "oracle", "extrapolated": True,
            "sample": "144 tiles (heads 0,9,18,27 first+last tile of each segment, 16 seeded) at tau*: "
                      "12.34 s; scaled by executed keys 1245622848/5036224"}
     study = {}
@@ -242,3 +243,13 @@ def test_record_of_a_full_run_fits_the_driver(monkeypatch):
     assert set(rec["ranking_study"]["precision_recall"]) == {"tile", "segment", "blocks", "qperm", "shared"}
     assert "tau_sweep" in full and "form_sweeps" in full and "by_tau" in full["ranking_study"]["tile"]
     assert json.loads(line) == rec
+
+
+def test_host_cpu_model_reads_the_first_model_name(tmp_path):
+    f = tmp_path / "cpuinfo"
+    f.write_text("processor\t: 0\nvendor_id\t: X\nmodel name\t: Some  CPU   @ 2.70GHz\n\n"
+                 "processor\t: 1\nmodel name\t: Other\n")
+    assert bench.host_cpu_model(str(f)) == "Some CPU @ 2.70GHz"
+    f.write_text("processor\t: 0\n")
+    assert bench.host_cpu_model(str(f)) is None
+    assert bench.host_cpu_model(str(tmp_path / "missing")) is None

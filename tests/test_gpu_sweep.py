@@ -1,0 +1,81 @@
+"""Seeded sweep over small random problems: every shape the C ABI accepts
+(head dim 64/128, query tiles 64/128, ragged last segments, 1-2 batches, GQA
+group sizes 1-4), both dtypes, every list form (per tile or per segment, keys
+or blocks, Q_perm, lists shared by a KV head's query heads) and thresholds
+from 0 to 0.1, each compared with the oracle on every tile: scores and lists
+bit for bit, executed-tile counts exact (near-tau ties excepted and re-checked)
+and outputs within the dtype's tolerance."""
+
+import numpy as np
+import pytest
+
+import long_context_prefill_amd as s2o
+import oracle
+from long_context_prefill_amd import synth
+
+N_CASES = 64
+SEED = 20261203
+
+
+def draw_cases(n=N_CASES, seed=SEED):
+    """(name, workload, lists, qperm, share, tau) for n seeded random problems."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = "f32" if i % 4 == 3 else "bf16"
+        d = int(rng.choice([64, 128]))
+        BM = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2]))
+        G = int(rng.choice([1, 2, 4]))
+        B = int(rng.choice([1, 2]))
+        S = BM * int(rng.integers(1, 5))
+        N = BM * int(rng.integers(2, 1536 // BM + 1))
+        lists = str(rng.choice(["tile", "segment", "tile_blocks", "segment_blocks"]))
+        qperm = dtype == "bf16" and bool(rng.random() < 0.3)
+        share = not qperm and bool(rng.random() < 0.3)
+        structure = str(rng.choice(["stripes", "stripes+band", "uniform"]))
+        tau = float(rng.choice([0.0, 1e-3, 1e-2, 0.1]))
+        name = (f"c{i}_{dtype}_d{d}_bm{BM}_b{B}_h{Hkv * G}x{Hkv}_n{N}_s{S}_{lists}"
+                f"{'_qperm' if qperm else ''}{'_shared' if share else ''}_{structure}_tau{tau:g}")
+        w = synth.custom_workload(B=B, Hq=Hkv * G, Hkv=Hkv, N=N, d=d, dtype=dtype, tile_m=BM, tile_n=64,
+                                  seg_len=S, structure=structure, n_stripes=max(N // 100, 4),
+                                  seed=3000 + i, name=name)
+        out.append((name, w, lists, qperm, share, tau))
+    return out
+
+
+CASES = draw_cases()
+
+
+def test_sweep_cases_are_valid_problems():
+    """Every drawn problem passes the ABI's validation (CPU, no GPU call)."""
+    import os
+    if not os.path.exists(s2o.LIB_PATH):
+        pytest.skip("libs2o.so not built")
+    forms = set()
+    for name, w, lists, qperm, share, tau in CASES:
+        p = s2o.problem(w.B, w.Hq, w.Hkv, w.N, w.d, 1 if w.dtype == "bf16" else 0, w.seg_len, w.tile_m,
+                        w.tile_n, w.scale, lists=lists, qperm=qperm, share_gqa=share)
+        assert s2o.check_problem(p) == 0, name
+        forms.add((w.dtype, lists, qperm, share))
+    # the sweep reaches both dtypes, every list granularity, Q_perm and shared lists
+    assert {f[0] for f in forms} == {"bf16", "f32"}
+    assert {f[1] for f in forms} == {"tile", "segment", "tile_blocks", "segment_blocks"}
+    assert any(f[2] for f in forms) and any(f[3] for f in forms)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_random_problem_matches_oracle(case):
+    from parity_util import GpuRun, assert_report, compare, say
+    name, w, lists, qperm, share, tau = case
+    say(f"sweep {name}")
+    x = synth.make_inputs(w)
+    run = GpuRun(w, x, lists=lists, qperm=qperm, share_gqa=share)
+    assert s2o.list_entries(run.p) == oracle.list_entries(run.po)
+    scores_o = oracle.scores_all(run.po, x["q"], x["k"])
+    assert np.array_equal(run.scores.cpu().numpy().view(np.uint32), scores_o.view(np.uint32))
+    assert np.array_equal(run.idx.cpu().numpy(), oracle.lists_all(run.po, scores_o))
+    o, ex = run.attn(tau)
+    tiles = [(b, h, t) for b in range(w.B) for h in range(w.Hq) for t in range(w.N // w.tile_m)]
+    assert_report(compare(run, tiles, tau, o, ex, check_lists=True), w.dtype)

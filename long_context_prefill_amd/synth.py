@@ -38,7 +38,7 @@ bit patterns.
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, Tuple
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -65,9 +65,12 @@ class Workload:
     structure: str  # "stripes", "stripes+band" or "uniform"
     n_stripes: int
     seed: int
+    softmax_scale: Optional[float] = None  # None: 1/sqrt(d)
 
     @property
     def scale(self) -> float:
+        if self.softmax_scale is not None:
+            return float(self.softmax_scale)
         return float(1.0 / np.sqrt(self.d))
 
 
@@ -183,7 +186,7 @@ def make_inputs(w: Workload, seed: int | None = None):
 
 def custom_workload(B=1, Hq=1, Hkv=1, N=256, d=64, dtype="f32", tile_m=64, tile_n=64,
                     seg_len=128, structure="stripes", n_stripes=8, seed=100,
-                    taus=(1e-3,), name="custom") -> Workload:
-    """A small workload for tests (shapes chosen by the caller)."""
+                    taus=(1e-3,), name="custom", scale=None) -> Workload:
+    """A small workload for tests (shapes chosen by the caller; scale None is 1/sqrt(d))."""
     return Workload(name, B, Hq, Hkv, N, d, dtype, tile_m, tile_n, seg_len,
-                    tuple(taus), structure, n_stripes, seed)
+                    tuple(taus), structure, n_stripes, seed, scale)

@@ -1,10 +1,11 @@
 """Seeded sweep over small random problems: every shape the C ABI accepts
-(head dim 64/128, query tiles 64/128, ragged last segments, 1-2 batches, GQA
-group sizes 1-4), both dtypes, every list form (per tile or per segment, keys
-or blocks, Q_perm, lists shared by a KV head's query heads) and thresholds
-from 0 to 0.1, each compared with the oracle on every tile: scores and lists
-bit for bit, executed-tile counts exact (near-tau ties excepted and re-checked)
-and outputs within the dtype's tolerance."""
+(head dim 64/128, query tiles 64/128, ragged last segments, 1-2 batches,
+GQA group sizes 1-4, softmax scales 0.25, 1 and 2.5 times 1/sqrt(d)), both
+dtypes, every list form (per tile or per segment, keys or blocks, Q_perm,
+lists shared by a KV head's query heads) and thresholds from 0 to 0.1, each
+compared with the oracle on every tile: scores and lists bit for bit,
+executed-tile counts exact (near-tau ties excepted and re-checked) and
+outputs within the dtype's tolerance."""
 
 import numpy as np
 import pytest
@@ -35,11 +36,12 @@ def draw_cases(n=N_CASES, seed=SEED):
         share = not qperm and bool(rng.random() < 0.3)
         structure = str(rng.choice(["stripes", "stripes+band", "uniform"]))
         tau = float(rng.choice([0.0, 1e-3, 1e-2, 0.1]))
+        sfac = float(rng.choice([0.25, 1.0, 2.5]))  # softmax scale as a multiple of 1/sqrt(d)
         name = (f"c{i}_{dtype}_d{d}_bm{BM}_b{B}_h{Hkv * G}x{Hkv}_n{N}_s{S}_{lists}"
-                f"{'_qperm' if qperm else ''}{'_shared' if share else ''}_{structure}_tau{tau:g}")
+                f"{'_qperm' if qperm else ''}{'_shared' if share else ''}_{structure}_tau{tau:g}_sc{sfac:g}")
         w = synth.custom_workload(B=B, Hq=Hkv * G, Hkv=Hkv, N=N, d=d, dtype=dtype, tile_m=BM, tile_n=64,
                                   seg_len=S, structure=structure, n_stripes=max(N // 100, 4),
-                                  seed=3000 + i, name=name)
+                                  seed=3000 + i, name=name, scale=sfac / np.sqrt(d))
         out.append((name, w, lists, qperm, share, tau))
     return out
 

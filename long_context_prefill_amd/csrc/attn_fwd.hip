@@ -609,6 +609,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         for (int i = 0; i < C::INSTR; ++i) vrows[i] = krows[i];
         if (k + 3 < total) fetch_rows(k + 3, krows);
 
+        // Wave priority (two workgroups per CU, so two waves per SIMD): the
+        // gather issue above and the end-of-chunk wait and barrier run at 0,
+        // the softmax bookkeeping and the QK^T phase at 1, the PV phase and
+        // the stop ballot at 2, so a wave in its PV phase issues ahead of one
+        // computing exponentials.  Only the issue order changes.
+        __builtin_amdgcn_s_setprio(1);
         const bool is_p2 = S2O && k >= n1;
         const int key0 = is_p2 ? 0 : base1 + k * BN;
         if (!is_p2 && g.causal && key0 + BN - 1 > wave_first) mask_chunk(s0, s1, key0, my_row, half);
@@ -626,6 +632,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         // (stale stage when k+1 == total; the result is unused then)
         qk(std::integral_constant<int, kst ^ 1>{}, sn0, sn1, s0, s1, m, true);
 
+        __builtin_amdgcn_s_setprio(2);
         // phase 2: O^T += V^T P^T for chunk k with the row sum
         float sum;
         {
@@ -663,6 +670,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_kernel_bf16(AttnParams a) {
         const bool wave_cont = is_p2 && __ballot(!(delta < a.tau * l)) != 0;
         const bool wave_ovf = !track && __ballot(!(delta < 0x1p64f)) != 0;
 
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's K_{k+2} / V_{k+1} pieces and indices landed
         if (lane == 0) flags[kst][wave] = (wave_cont ? 1 : 0) | (wave_ovf ? 2 : 0);
         __syncthreads();

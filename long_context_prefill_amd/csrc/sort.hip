@@ -753,13 +753,15 @@ __global__ __launch_bounds__(THREADS, 4) void queued_range_kernel(const u32x2 *_
 // Ranges left over by queued_range_kernel (crowded sub-buckets, or above CAP):
 // each workgroup takes them in turn; one that fits in LDS is sorted there
 // with stable LSD passes, a larger one with stable LSD passes through global
-// scratch, CAP entries at a time in order.
+// scratch, CAP entries at a time in order.  The scratch copy of a range sits
+// at the range's own offset (slot_len = 0: scratch as long as the lists), or
+// in the workgroup's slot of slot_len entries (slot_len >= the longest list).
 __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ pairs,
                                                            u32x2 *__restrict__ scratch,
                                                            int32_t *__restrict__ idx,
                                                            const Overflow *__restrict__ queue,
                                                            const int32_t *__restrict__ queue_len,
-                                                           Geometry g) {
+                                                           Geometry g, int64_t slot_len) {
     __shared__ u32x2 stage[CAP];
     __shared__ int cnt[NWAVES][NB];
     __shared__ int dtot[NB];
@@ -790,7 +792,8 @@ __global__ __launch_bounds__(THREADS) void overflow_kernel(u32x2 *__restrict__ p
             __syncthreads();  // the next range reuses the LDS
             continue;
         }
-        u32x2 *src = pairs + base, *dst = scratch + base;
+        u32x2 *src = pairs + base;
+        u32x2 *dst = scratch + (slot_len > 0 ? (int64_t)blockIdx.x * slot_len : base);
         uint32_t kmin = 0xFFFFFFFFu, pmin = 0xFFFFFFFFu;
         for (int i = tid; i < m; i += THREADS) {
             kmin = min(kmin, src[i].x);
@@ -879,6 +882,7 @@ int range_chunk(const Geometry &g) {
 
 struct SortWs {
     u32x2 *pairs, *scratch;
+    int64_t slot_len;  // 0: scratch mirrors pairs; else one slot of this many entries per overflow workgroup
     int32_t *hist, *blk_list, *bstart, *queue_len;
     Buckets *list_bk;
     Overflow *queue, *queue2;
@@ -896,8 +900,12 @@ SortWs carve(const Geometry &g, void *base) {
     char *p = reinterpret_cast<char *>(base);
     w.pairs = reinterpret_cast<u32x2 *>(p + off);
     off += align256(n * 8);
+    // the overflow kernel's scratch: a copy of the lists, or one slot per
+    // workgroup as long as the longest list, whichever is smaller
+    const int64_t slots = (int64_t)OVERFLOW_GRID * max_list_len(g);
+    w.slot_len = slots < n ? max_list_len(g) : 0;
     w.scratch = reinterpret_cast<u32x2 *>(p + off);
-    off += align256(n * 8);
+    off += align256((size_t)(w.slot_len > 0 ? slots : n) * 8);
     w.hist = reinterpret_cast<int32_t *>(p + off);
     off += align256((size_t)nblocks * NB * 4);
     w.blk_list = reinterpret_cast<int32_t *>(p + off);
@@ -934,7 +942,7 @@ hipError_t run_sort(const Geometry &g, const float *scores, int32_t *idx, const 
     hipLaunchKernelGGL(queued_range_kernel, dim3(QUEUED_GRID), dim3(THREADS), 0, stream, w.pairs, idx, w.queue,
                        w.queue_len, w.queue2, w.queue_len + 1, g);
     hipLaunchKernelGGL(overflow_kernel, dim3(OVERFLOW_GRID), dim3(THREADS), 0, stream, w.pairs, w.scratch, idx,
-                       w.queue2, w.queue_len + 1, g);
+                       w.queue2, w.queue_len + 1, g, w.slot_len);
     return hipGetLastError();
 }
 

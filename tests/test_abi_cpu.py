@@ -120,6 +120,13 @@ def test_workspace_sizes():
     # longer lists: (key, position) pairs and their scratch copy, 16 bytes per entry
     p = base_problem(seq_len=16384, seg_len=4096)
     assert s2o.build_index_workspace_bytes(p) >= 16 * s2o.list_entries(p)
+    # many lists: the scratch is one slot per overflow workgroup (1024 x the
+    # longest list) once that is smaller than a copy of every list
+    p = s2o.problem(1, 32, 8, 131072, 128, 1, 8192, 128, 64)
+    n, longest = s2o.list_entries(p), 15 * 8192
+    ws = s2o.build_index_workspace_bytes(p)
+    assert 8 * n + 8 * 1024 * longest <= ws < 8 * n + 8 * 1024 * longest + n  # + histograms and queues
+    assert ws < 9 * n
     # block lists: the mean key of every block joins the pooled queries
     p = base_problem(lists="tile_blocks")
     assert s2o.score_workspace_bytes(p) == 1 * 4 * 8 * 128 * 4 + 1 * 2 * (1024 // 64) * 128 * 4

@@ -519,6 +519,26 @@ def test_build_index_crafted_scores(kind, lists):
     assert np.array_equal(idx.cpu().numpy(), oracle.lists_all(po, sc))
 
 
+@pytest.mark.parametrize("kind", ["all_equal", "few_values"])
+def test_build_index_overflow_slots(kind):
+    """Enough lists that the overflow kernel's scratch is one slot per
+    workgroup (1024 x the longest list) instead of a copy of every list, with
+    scores that send whole lists through its global LSD passes."""
+    N, S, BM, Hq = 32768, 8192, 128, 16
+    p = s2o.problem(1, Hq, 1, N, 64, 1, S, BM, 64)
+    po = oracle.problem(1, Hq, 1, N, 64, "bf16", S, BM, 64, 0.125)
+    n = s2o.list_entries(p)
+    longest = (N // S - 1) * S
+    assert n > 1024 * longest  # slot mode
+    assert s2o.build_index_workspace_bytes(p) < 16 * n
+    rng = np.random.default_rng(7)
+    sc = _crafted_scores(kind, n, rng)
+    say(f"build_index overflow slots kind={kind} n={n}")
+    idx = s2o.s2o_build_index(p, torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), oracle.lists_all(po, sc))
+
+
 # ------------------------------------------------------------- block lists ---
 # Entries are blocks of BN keys scored by their mean key; pass-2 chunk c is the
 # c-th listed block (the block-granularity counterpart of the method).

@@ -19,13 +19,12 @@
 //      contiguous range of the final order, and equal scores share a bucket;
 //      the sample only affects how evenly the buckets fill.  plan (per list:
 //      sample bounds) -> hist (per block, LDS atomics) -> scan (per list) ->
-//      scatter (per block: stable rank by a wave-level multisplit, staged in
-//      LDS, written as contiguous bucket runs of (key, position) pairs; each
-//      XCD takes a contiguous share of the blocks, so the partial cache lines
-//      where neighbouring blocks' runs meet are merged in one L2).  Within a
-//      bucket, positions ascend; the steps below do not rely on it (the
-//      multisplit is kept because LDS atomics on the few crowded buckets of a
-//      peaked score distribution serialize and cost more than it).
+//      scatter (per block: a slot in its digit's run for every entry from LDS
+//      atomics on the block's digit counters, staged in LDS, written as
+//      contiguous bucket runs of (key, position) pairs; each XCD takes a
+//      contiguous share of the blocks, so the partial cache lines where
+//      neighbouring blocks' runs meet are merged in one L2).  The order
+//      inside a bucket is arbitrary; the steps below do not rely on it.
 //   2. range sort.  Each workgroup owns the buckets that start inside its
 //      chunk of C output positions, i.e. a contiguous range of the list, and
 //      orders it without radix passes: NSB sub-buckets of equal score width
@@ -264,7 +263,10 @@ __global__ __launch_bounds__(NB) void scan_kernel(int32_t *__restrict__ hist, in
     if (v == 0) bs[NB] = (int32_t)L.len;
 }
 
-// Per block: stable scatter into bucket runs of (key, position) pairs.
+// Per block: scatter into bucket runs of (key, position) pairs.  LDS atomics on
+// one set of digit counters hand each entry a slot in its digit's run, in no
+// particular order (the range sort orders every range by (key, position)
+// itself); the entries are staged in LDS by digit and written as runs.
 template <int E>
 __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restrict__ scores,
                                                           const int32_t *__restrict__ blk_list,
@@ -273,9 +275,8 @@ __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restric
                                                           u32x2 *__restrict__ pairs, Geometry g, int64_t nblocks) {
     constexpr int NWV = E >= 256 ? NWAVES : E / 64;  // waves holding entries
     constexpr int ROUNDS = E / (64 * NWV);           // wave w owns [w*E/NWV, (w+1)*E/NWV)
-    __shared__ int cnt[NWAVES][NB];  // per-wave digit counters, then staging offsets
-    __shared__ int dstart[NB];       // first staged position of each digit
-    __shared__ int dglob[NB];        // run start of each digit relative to the block, minus dstart
+    __shared__ int cnt[NB];          // digit counts, then each digit's first staged position
+    __shared__ int dglob[NB];        // run start of each digit relative to the block, minus its staged start
     __shared__ u32x2 stage[E];       // (key, position) sorted by digit
     __shared__ uint8_t sdig[E];
     // XCD-aware order: block ids are dispatched round-robin over the 8 XCDs;
@@ -285,8 +286,10 @@ __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restric
     const int64_t blk = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
     if (blk >= nblocks) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < NWAVES * NB; i += THREADS) (&cnt[0][0])[i] = 0;
-    for (int v = tid; v < NB; v += THREADS) dglob[v] = hist[blk * NB + v];
+    for (int v = tid; v < NB; v += THREADS) {
+        cnt[v] = 0;
+        dglob[v] = hist[blk * NB + v];
+    }
     const Buckets bk = list_bk[blk_list[blk]];
     __syncthreads();
     const int64_t base = blk * E;
@@ -301,38 +304,17 @@ __global__ __launch_bounds__(THREADS) void scatter_kernel(const float *__restric
 #pragma unroll
         for (int r = 0; r < ROUNDS; ++r) {
             dig[r] = bucket_digit(x[r], bk);
-            const uint64_t peers = match_digit(dig[r]);
-            const int before = cnt[wave][dig[r]];  // read by all peers before the leader updates
-            rank[r] = before + __popcll(peers & lanemask_lt());
-            if ((peers & lanemask_lt()) == 0) cnt[wave][dig[r]] = before + __popcll(peers);
+            rank[r] = atomicAdd(&cnt[dig[r]], 1);  // a slot in the digit's run, in no particular order
         }
     }
     __syncthreads();
-    for (int v = tid; v < NB; v += THREADS) {
-        int s = 0;
-#pragma unroll
-        for (int w = 0; w < NWAVES; ++w) {
-            const int c = cnt[w][v];
-            cnt[w][v] = s;
-            s += c;
-        }
-        dstart[v] = s;
-    }
+    scan256(cnt);
     __syncthreads();
-    scan256(dstart);
-    __syncthreads();
-    // fold the digit starts into the per-wave offsets and the run starts, so
-    // each entry needs one lookup on the way in and one on the way out
-    for (int v = tid; v < NB; v += THREADS) {
-#pragma unroll
-        for (int w = 0; w < NWAVES; ++w) cnt[w][v] += dstart[v];
-        dglob[v] -= dstart[v];
-    }
-    __syncthreads();
+    for (int v = tid; v < NB; v += THREADS) dglob[v] -= cnt[v];
     if (wave < NWV) {
 #pragma unroll
         for (int r = 0; r < ROUNDS; ++r) {
-            const int p = cnt[wave][dig[r]] + rank[r];
+            const int p = cnt[dig[r]] + rank[r];
             u32x2 pr;
             pr.x = desc_key(x[r]);
             pr.y = (uint32_t)(pos0 + wave * (E / NWV) + 64 * r + lane);

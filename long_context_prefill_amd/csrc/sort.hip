@@ -1,4 +1,4 @@
-// Segmented stable sort of the index lists, gfx950.
+// Segmented sort of the index lists by (score descending, position), gfx950.
 //
 // "S2O: Early Stopping for Sparse Attention via Online Permutation",
 // gist.science technical summary, "Classement par Segment" (KV_perm): the
@@ -11,7 +11,7 @@
 // entries (E = largest power of two dividing S, at most 4096) that never
 // straddle two lists.  Two data passes instead of four LSD passes:
 //
-//   1. bucket pass (one stable MSD step).  Each list's scores are split into
+//   1. bucket pass (one MSD step).  Each list's scores are split into
 //      256 buckets of equal width between the minimum and maximum of a sample
 //      of the list (every 16th run of 64 scores), highest values first; scores
 //      outside the sampled range join the end buckets.  The bucket function is

@@ -91,7 +91,34 @@ def counter_report(paths):
             "trans_per_mfma": avg["SQ_INSTS_VALU_TRANS_F32"] / avg["SQ_INSTS_MFMA"],
             "lds_insts_per_mfma": avg["SQ_INSTS_LDS"] / avg["SQ_INSTS_MFMA"],
         }
+        out[n].update(mfma_work(avg))
     return out
+
+
+# SQ_INSTS_VALU_MFMA_MOPS_* count matrix-core operations in units of 512
+# (one multiply-add is 2 flop).
+MOPS_UNIT = 512
+
+
+def mfma_work(avg):
+    """Matrix-core flops by type and GPU-active cycles, when collected."""
+    d = {}
+    for t in ("BF16", "F32"):
+        c = f"SQ_INSTS_VALU_MFMA_MOPS_{t}"
+        if c in avg:
+            d[f"mfma_flop_{t.lower()}"] = avg[c] * MOPS_UNIT
+    if "GRBM_GUI_ACTIVE" in avg:
+        d["gui_active_cycles"] = avg["GRBM_GUI_ACTIVE"]
+    return d
+
+
+def print_mfma_work(d):
+    for t in ("bf16", "f32"):
+        if f"mfma_flop_{t}" in d:
+            print(f"  matrix-core work ({t})           {d[f'mfma_flop_{t}']:10.4g} flop "
+                  f"(SQ_INSTS_VALU_MFMA_MOPS_{t.upper()} x {MOPS_UNIT})")
+    if "gui_active_cycles" in d:
+        print(f"  GPU active cycles                {d['gui_active_cycles']:10.4g} (GRBM_GUI_ACTIVE)")
 
 
 # MI355X has 256 CUs; a wave64 vector instruction holds its SIMD for 4 cycles
@@ -125,6 +152,7 @@ def kernel_counter_table(paths, kernels):
                 d["lds_busy"] = avg["SQ_LDS_IDX_ACTIVE"] / CUS / se
         if "SQ_LDS_IDX_ACTIVE" in avg and "SQ_LDS_BANK_CONFLICT" in avg and avg["SQ_LDS_IDX_ACTIVE"] > 0:
             d["lds_bank_conflict_share"] = avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_LDS_IDX_ACTIVE"]
+        d.update(mfma_work(avg))
         if all(c in avg for c in ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY")):
             w = avg["SQ_WAVE_CYCLES"]
             d["wave_issuing"] = avg["SQ_ACTIVE_INST_ANY"] / w
@@ -197,6 +225,7 @@ def main_kernel_counters(a):
             print(f"  LDS busy                           {100 * d['lds_busy']:6.1f} % of CU cycles")
         if "lds_bank_conflict_share" in d:
             print(f"  bank conflicts                     {100 * d['lds_bank_conflict_share']:6.1f} % of LDS-active cycles")
+        print_mfma_work(d)
         if "wave_issuing" in d:
             print(f"  wave time issuing / waiting for an issue slot / at waits and barriers: "
                   f"{100 * d['wave_issuing']:.0f} / {100 * d['wave_waiting_issue']:.0f} / "
@@ -218,7 +247,9 @@ def main_counters(a):
               f"{100 * r['wave_issuing']:.0f} / {100 * r['wave_waiting_issue']:.0f} / "
               f"{100 * r['wave_waiting_counters_barrier']:.0f} %")
         print(f"  per MFMA: {r['valu_insts_per_mfma']:.2f} other VALU ({r['trans_per_mfma']:.2f} "
-              f"transcendental), {r['lds_insts_per_mfma']:.2f} LDS instructions\n")
+              f"transcendental), {r['lds_insts_per_mfma']:.2f} LDS instructions")
+        print_mfma_work(r)
+        print()
     if a.json_out:
         src = sources_hash(a.source) if a.source else None
         out = {n: {k: v for k, v in r.items() if k != "counters"} for n, r in rep.items()}

@@ -71,3 +71,21 @@ def test_l2_report_scales_by_the_copy(tmp_path):
     assert abs(r["dram_write_bytes"] - 16 * 64) < 1e-9
     assert abs(out[ps.short(copy)]["dram_read_bytes"] - 128 * 1024) < 1e-9
     assert abs(out[ps.short(copy)]["dram_write_bytes"] - 128 * 1024) < 1e-9
+
+
+def test_matrix_core_work_from_the_op_counters(tmp_path):
+    """SQ_INSTS_VALU_MFMA_MOPS_* count operations in units of 512: a 32x32x16
+    bf16 MFMA (32768 flop) is 64 of them, so 128 of them per executed tile give
+    the tile's 4.19 MFLOP; GRBM_GUI_ACTIVE passes through."""
+    path = tmp_path / "c.csv"
+    attn = "void s2o::(anonymous namespace)::attn_kernel_bf16<128, 4, true>(x)"
+    score = "void s2o::(anonymous namespace)::score_mfma_kernel<__bf16, 128, 32, 2>(x)"
+    tiles = 1000
+    _counter_csv(path, [(attn, "SQ_INSTS_VALU_MFMA_MOPS_BF16", tiles * 128 * 64.0),
+                        (attn, "GRBM_GUI_ACTIVE", 5.0e6),
+                        (score, "SQ_INSTS_VALU_MFMA_MOPS_F32", 8.0)])
+    d = ps.mfma_work(ps.kernel_counter_table([str(path)], ["s2o_attn_fwd (S2O schedule)"])
+                     ["s2o_attn_fwd (S2O schedule)"]["counters"])
+    assert d["mfma_flop_bf16"] == tiles * 4 * 128 * 64 * 128 and d["gui_active_cycles"] == 5.0e6
+    s = ps.kernel_counter_table([str(path)], ["score_mfma_kernel (s2o_score)"])["score_mfma_kernel (s2o_score)"]
+    assert s["mfma_flop_f32"] == 8 * 512 and "mfma_flop_bf16" not in s
